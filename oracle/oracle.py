@@ -1,0 +1,126 @@
+"""ctypes front end of the fp64 C oracle (``oracle.c``).  Test infrastructure only.
+
+The C source states the definition it computes.  This wrapper only compiles
+it with gcc and marshals numpy buffers; it does no arithmetic of its own.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (-O2, no fast-math)."""
+    global _lib
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared",
+                               "-fno-fast-math", _SRC, "-o", tmp, "-lpthread", "-lm"])
+        os.replace(tmp, _LIB)
+        _lib = None
+    return _LIB
+
+
+def _open(path: str):
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    i32, i64 = ctypes.c_int, ctypes.c_int64
+    lib.oracle_decode_attn.argtypes = [i32, i32, i32, i32, i32, i32, i64, i64,
+                                       ctypes.c_double, P, P, P, P, P, P, P, P, P,
+                                       P, i32, P, P, i32]
+    lib.oracle_decode_attn.restype = i32
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        _lib = _open(_LIB)
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def decode_attn(q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path, beam_len,
+                row_offset, scale: Optional[float] = None,
+                rows: Optional[Sequence[int]] = None, n_threads: Optional[int] = None):
+    """fp64 attention of each packed row over its request's context ++ its BeamPath tokens.
+
+    bf16 tensors are uint16 bit arrays in the library's layouts:
+    q [R][Hq][D], ctx_k/ctx_v [B][ctx_cap][Hkv][D], beam_k/beam_v
+    [B][beam_cap][Hkv][D]; beam_path [R][T_cap] int32; ctx_len, beam_len [B],
+    row_offset [B+1] int32.  Returns (out [n][Hq][D] float64, lse [n][Hq]
+    float64) for ``rows`` (all R rows by default), lse in natural log.
+    """
+    return _call(_load(), q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path, beam_len,
+                 row_offset, scale, rows, n_threads)
+
+
+def from_library(path: str):
+    """``decode_attn`` bound to another build of oracle.c (the tests compile
+    deliberately broken copies to show that the pins reject them)."""
+    lib = _open(path)
+
+    def fn(q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path, beam_len, row_offset,
+           scale=None, rows=None, n_threads=None):
+        return _call(lib, q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path, beam_len,
+                     row_offset, scale, rows, n_threads)
+    return fn
+
+
+def _call(lib, q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path, beam_len, row_offset,
+          scale, rows, n_threads):
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    ctx_k = np.ascontiguousarray(ctx_k, dtype=np.uint16)
+    ctx_v = np.ascontiguousarray(ctx_v, dtype=np.uint16)
+    beam_k = np.ascontiguousarray(beam_k, dtype=np.uint16)
+    beam_v = np.ascontiguousarray(beam_v, dtype=np.uint16)
+    ctx_len = np.ascontiguousarray(ctx_len, dtype=np.int32)
+    beam_len = np.ascontiguousarray(beam_len, dtype=np.int32)
+    row_offset = np.ascontiguousarray(row_offset, dtype=np.int32)
+    beam_path = np.ascontiguousarray(beam_path, dtype=np.int32)
+    R, Hq, D = q.shape
+    B, ctx_cap, Hkv, D2 = ctx_k.shape
+    assert D2 == D and beam_k.shape[0] == B and beam_k.shape[2:] == (Hkv, D)
+    assert ctx_v.shape == ctx_k.shape and beam_v.shape == beam_k.shape
+    assert beam_path.ndim == 2 and beam_path.shape[0] == R
+    T_cap = beam_path.shape[1]
+    beam_cap = beam_k.shape[1]
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(D))
+    rows_arr = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+    n = R if rows_arr is None else int(rows_arr.size)
+    out = np.zeros((n, Hq, D), dtype=np.float64)
+    lse = np.zeros((n, Hq), dtype=np.float64)
+    if n_threads is None:
+        n_threads = os.cpu_count() or 1
+    st = lib.oracle_decode_attn(B, R, Hq, Hkv, D, T_cap, ctx_cap, beam_cap, float(scale),
+                                _ptr(q), _ptr(ctx_k), _ptr(ctx_v), _ptr(ctx_len), _ptr(beam_k),
+                                _ptr(beam_v), _ptr(beam_path), _ptr(beam_len), _ptr(row_offset),
+                                _ptr(rows_arr), n, _ptr(out), _ptr(lse), int(n_threads))
+    if st != 0:
+        raise RuntimeError(f"oracle_decode_attn failed with status {st}")
+    return out, lse
+
+
+def decode_attn_inputs(inp, rows=None, n_threads=None):
+    """Run the oracle on a generated ``Inputs`` object."""
+    return decode_attn(inp.q, inp.ctx_k, inp.ctx_v, inp.ctx_len, inp.beam_k, inp.beam_v,
+                       inp.beam_path, inp.beam_len, inp.row_offset, scale=inp.scale,
+                       rows=rows, n_threads=n_threads)

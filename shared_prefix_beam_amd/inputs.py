@@ -1,0 +1,285 @@
+"""Seeded synthetic inputs for large-beam decode attention.
+
+This module only draws inputs: random bf16 tensors, ragged lengths, beam
+parent chains and the resolved BeamPath table.  It holds none of the attention
+arithmetic, so both the HIP path and the CPU oracle can take their inputs from
+here without sharing any of the method.
+
+Data model (GR-Inference blog, section on system design; xGR review, section
+"xAttention", KV cache management):
+
+* ContextKV: one long prefill KV per request, shared by all of its beams.
+  Layout ``[B][ctx_cap][Hkv][D]`` bf16; tokens ``j >= ctx_len[b]`` are padding.
+* BeamKV: the short per-beam KV written during decode, one token per
+  (step, live beam).  Layout ``[B][beam_cap][Hkv][D]`` bf16, step-major:
+  step ``s``, beam slot ``k`` lives at flat index ``s * W_cap + k``.  One extra
+  slot at index ``T_cap * W_cap`` is always padding; unused BeamPath entries
+  point at it.
+* BeamPath: for each query row (one live beam of one request) the flat BeamKV
+  indices of the tokens on its ancestry chain, step 0 first, its own current
+  token last.  Layout ``[R][T_cap]`` int32; entries ``s >= beam_len[b]`` are
+  padding.
+* Rows of all requests are packed: request ``b`` owns rows
+  ``row_offset[b] .. row_offset[b+1]-1``; q is ``[R][Hq][D]`` bf16.
+
+Every padding element of every bf16 buffer is a quiet NaN, so a kernel that
+reads outside the valid region produces NaN in its output.
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+BF16_NAN = np.uint16(0x7FC0)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """Shape and value recipe of one synthetic decode-attention call."""
+
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    W: Sequence[int]            # beams (query rows) per request
+    ctx: tuple                  # ("fixed", L) or ("uniform", lo, hi), inclusive
+    T: tuple                    # ("fixed", T) or ("uniform", lo, hi), inclusive
+    seed: int
+    q_std: float = 1.0
+    kv_std: float = 1.0
+    dup_frac: float = 0.0       # fraction of beams that copy one beam's full path row
+    grow_steps: bool = False    # per-step beam width grows from W/8 to W
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+
+# The five workloads: Qwen3 attention shapes (0.6B/1.7B: Hq=16, Hkv=8;
+# 4B: Hq=32, Hkv=8; head dim 128), contexts of 1k-4k tokens, beam widths
+# 4-900 and 2-5 decode tokens, as on the GR-Inference and SID-GR pages.
+WORKLOADS: Dict[int, Workload] = {
+    1: Workload("tiny_b1_l64_w4_g2_d64", B=1, Hq=2, Hkv=1, D=64, W=(4,),
+                ctx=("fixed", 64), T=("fixed", 3), seed=101),
+    2: Workload("qwen3_0.6b_b8_l1024_w128", B=8, Hq=16, Hkv=8, D=128, W=(128,) * 8,
+                ctx=("fixed", 1024), T=("fixed", 3), seed=202),
+    3: Workload("qwen3_1.7b_b16_l512-4096_w256_ragged", B=16, Hq=16, Hkv=8, D=128,
+                W=(256,) * 16, ctx=("uniform", 512, 4096), T=("uniform", 2, 5),
+                seed=303, q_std=0.5),
+    4: Workload("qwen3_0.6b_b4_l2048_w900_dup30", B=4, Hq=16, Hkv=8, D=128,
+                W=(900,) * 4, ctx=("fixed", 2048), T=("fixed", 3), seed=404,
+                dup_frac=0.3),
+    5: Workload("qwen3_4b_b6_l1024-3072_w20-900_grow", B=6, Hq=32, Hkv=8, D=128,
+                W=(20, 128, 256, 512, 512, 900), ctx=("uniform", 1024, 3072),
+                T=("fixed", 5), seed=505, grow_steps=True),
+}
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest even); return raw bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bits to float32."""
+    return (h.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def step_widths(W: int, T: int, grow: bool) -> List[int]:
+    """Live beams at each decode step s = 0..T-1; the last step has W beams.
+
+    With ``grow`` the width rises linearly from W/8 at step 0 to W at the last
+    step (floor, at least 1); otherwise every step has W beams.
+    """
+    if not grow or T <= 1:
+        return [W] * T
+    return [max(1, (W * (T - 1 + 7 * s)) // (8 * (T - 1))) for s in range(T)]
+
+
+@dataclasses.dataclass
+class Inputs:
+    """One generated call.  bf16 tensors are uint16 bit patterns."""
+
+    wl: Workload
+    q: np.ndarray           # [R][Hq][D] u16
+    ctx_k: np.ndarray       # [B][ctx_cap][Hkv][D] u16
+    ctx_v: np.ndarray
+    beam_k: np.ndarray      # [B][beam_cap][Hkv][D] u16
+    beam_v: np.ndarray
+    ctx_len: np.ndarray     # [B] i32
+    beam_len: np.ndarray    # [B] i32
+    row_offset: np.ndarray  # [B+1] i32
+    beam_path: np.ndarray   # [R][T_cap] i32
+    widths: List[List[int]]                 # per request, per step live beams
+    parents: List[List[np.ndarray]]         # per request, per step s>=1: parent slot of each slot
+    dup_src: List[Optional[int]]            # per request: beam whose path row was copied
+    dup_rows: List[np.ndarray]              # per request: beams that copied it
+    W_cap: int
+    T_cap: int
+
+    @property
+    def B(self) -> int:
+        return self.wl.B
+
+    @property
+    def R(self) -> int:
+        return int(self.row_offset[-1])
+
+    @property
+    def ctx_cap(self) -> int:
+        return self.ctx_k.shape[1]
+
+    @property
+    def beam_cap(self) -> int:
+        return self.beam_k.shape[1]
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.wl.D))
+
+    def arrays(self) -> Dict[str, np.ndarray]:
+        return dict(q=self.q, ctx_k=self.ctx_k, ctx_v=self.ctx_v, beam_k=self.beam_k,
+                    beam_v=self.beam_v, ctx_len=self.ctx_len, beam_len=self.beam_len,
+                    row_offset=self.row_offset, beam_path=self.beam_path)
+
+    def digest(self) -> str:
+        """SHA-256 over every buffer, to pin generator reproducibility."""
+        h = hashlib.sha256()
+        for k, v in self.arrays().items():
+            h.update(k.encode())
+            h.update(np.ascontiguousarray(v).tobytes())
+        return h.hexdigest()
+
+
+def _draw_len(rng: np.random.Generator, spec: tuple, B: int) -> np.ndarray:
+    if spec[0] == "fixed":
+        return np.full(B, spec[1], dtype=np.int32)
+    lo, hi = spec[1], spec[2]
+    return rng.integers(lo, hi + 1, size=B).astype(np.int32)
+
+
+def _cap(spec: tuple) -> int:
+    return spec[1] if spec[0] == "fixed" else spec[2]
+
+
+def _normal_bf16(rng: np.random.Generator, shape, std: float) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return to_bf16_bits(x)
+
+
+def generate(wl: Workload, seed: Optional[int] = None) -> Inputs:
+    """Draw one call of workload ``wl``.
+
+    Draw order is fixed: lengths, q, ctx_k, ctx_v, beam_k, beam_v, parent
+    chains, duplicate-path choices.  Padding is poisoned with bf16 NaN after
+    all draws, so the valid values do not depend on the padding.
+    """
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    ctx_len = _draw_len(rng, wl.ctx, wl.B)
+    beam_len = _draw_len(rng, wl.T, wl.B)
+    return _build(rng, wl, ctx_len, beam_len, _cap(wl.ctx), _cap(wl.T))
+
+
+def custom(B: int, Hq: int, Hkv: int, D: int, W: Sequence[int], ctx_len: Sequence[int],
+           beam_len: Sequence[int], seed: int, ctx_cap: Optional[int] = None,
+           T_cap: Optional[int] = None, q_std: float = 1.0, grow_steps: bool = False,
+           dup_frac: float = 0.0) -> Inputs:
+    """Inputs with explicit per-request lengths (edge cases, small parity shapes)."""
+    ctx_len = np.asarray(ctx_len, dtype=np.int32)
+    beam_len = np.asarray(beam_len, dtype=np.int32)
+    ctx_cap = max(int(ctx_len.max()), 1) if ctx_cap is None else ctx_cap
+    T_cap = max(int(beam_len.max()), 1) if T_cap is None else T_cap
+    wl = Workload(f"custom_s{seed}", B=B, Hq=Hq, Hkv=Hkv, D=D, W=tuple(W),
+                  ctx=("fixed", ctx_cap), T=("fixed", T_cap), seed=seed, q_std=q_std,
+                  grow_steps=grow_steps, dup_frac=dup_frac)
+    return _build(np.random.default_rng(seed), wl, ctx_len, beam_len, ctx_cap, T_cap)
+
+
+def _build(rng: np.random.Generator, wl: Workload, ctx_len: np.ndarray,
+           beam_len: np.ndarray, ctx_cap: int, T_cap: int) -> Inputs:
+    B, Hq, Hkv, D = wl.B, wl.Hq, wl.Hkv, wl.D
+    assert Hq % Hkv == 0 and len(wl.W) == B
+    assert int(ctx_len.max(initial=0)) <= ctx_cap and int(beam_len.max(initial=0)) <= T_cap
+    W = np.asarray(wl.W, dtype=np.int64)
+    row_offset = np.zeros(B + 1, dtype=np.int32)
+    row_offset[1:] = np.cumsum(W)
+    R = int(row_offset[-1])
+    W_cap = max(int(W.max()), 1)
+    beam_cap = T_cap * W_cap + 1          # + one always-padding slot
+    pad_slot = T_cap * W_cap
+
+    q = _normal_bf16(rng, (R, Hq, D), wl.q_std)
+    ctx_k = _normal_bf16(rng, (B, ctx_cap, Hkv, D), wl.kv_std)
+    ctx_v = _normal_bf16(rng, (B, ctx_cap, Hkv, D), wl.kv_std)
+    beam_k = _normal_bf16(rng, (B, beam_cap, Hkv, D), wl.kv_std)
+    beam_v = _normal_bf16(rng, (B, beam_cap, Hkv, D), wl.kv_std)
+
+    beam_path = np.full((R, T_cap), pad_slot, dtype=np.int32)
+    widths: List[List[int]] = []
+    parents: List[List[np.ndarray]] = []
+    for b in range(B):
+        T = int(beam_len[b])
+        ws = step_widths(int(W[b]), T, wl.grow_steps)
+        widths.append(ws)
+        par = [np.zeros(0, dtype=np.int64)]
+        for s in range(1, T):
+            par.append(rng.integers(0, ws[s - 1], size=ws[s]))
+        parents.append(par)
+        # walk every final beam back to step 0 (vectorised over beams)
+        k = np.arange(W[b], dtype=np.int64)
+        rows = beam_path[row_offset[b]:row_offset[b + 1]]
+        for s in range(T - 1, -1, -1):
+            rows[:, s] = s * W_cap + k
+            if s > 0:
+                k = par[s][k]
+
+    dup_src: List[Optional[int]] = []
+    dup_rows: List[np.ndarray] = []
+    for b in range(B):
+        Wb = int(W[b])
+        n_dup = min(int(round(wl.dup_frac * Wb)), max(Wb - 1, 0))
+        if n_dup == 0:
+            dup_src.append(None)
+            dup_rows.append(np.zeros(0, dtype=np.int64))
+            continue
+        src = int(rng.integers(0, Wb))
+        others = np.delete(np.arange(Wb), src)
+        sel = np.sort(rng.choice(others, size=n_dup, replace=False))
+        r0 = int(row_offset[b])
+        beam_path[r0 + sel] = beam_path[r0 + src]
+        dup_src.append(src)
+        dup_rows.append(sel)
+
+    # poison padding
+    for b in range(B):
+        ctx_k[b, ctx_len[b]:] = BF16_NAN
+        ctx_v[b, ctx_len[b]:] = BF16_NAN
+        live = np.zeros(beam_cap, dtype=bool)
+        for s, ws in enumerate(widths[b]):
+            live[s * W_cap: s * W_cap + ws] = True
+        beam_k[b, ~live] = BF16_NAN
+        beam_v[b, ~live] = BF16_NAN
+
+    return Inputs(wl=wl, q=q, ctx_k=ctx_k, ctx_v=ctx_v, beam_k=beam_k, beam_v=beam_v,
+                  ctx_len=np.asarray(ctx_len, dtype=np.int32),
+                  beam_len=np.asarray(beam_len, dtype=np.int32), row_offset=row_offset,
+                  beam_path=beam_path, widths=widths, parents=parents,
+                  dup_src=dup_src, dup_rows=dup_rows, W_cap=W_cap, T_cap=T_cap)
+
+
+def unique_beam_rows(inp: Inputs) -> List[int]:
+    """Per request: number of distinct BeamKV tokens referenced by its paths."""
+    out = []
+    for b in range(inp.B):
+        r0, r1 = int(inp.row_offset[b]), int(inp.row_offset[b + 1])
+        T = int(inp.beam_len[b])
+        out.append(int(np.unique(inp.beam_path[r0:r1, :T]).size) if T > 0 else 0)
+    return out
