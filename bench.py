@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Benchmark of the large-beam decode-attention hot path on one MI355X.
+
+One step = one gr_decode_attn call over a whole batch: the shared-context
+stage, the per-beam BeamPath stage and the log-sum-exp merge for every
+(request, beam, head).  Inputs are seeded synthetic tensors with the
+workloads' shapes, resident in HBM before timing starts; consecutive steps
+rotate over enough copies of the inputs (more than twice the 256 MB
+Infinity Cache) that every step reads them from HBM.
+
+Prints ONE JSON line.  The headline workload is the Qwen3-0.6B attention
+shape at 128 beams (B=8, ctx 1024, HBM-bound); the 900-beam workload
+(MFMA-bound) is measured the same way and reported under "secondary".
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from shared_prefix_beam_amd import inputs as I  # noqa: E402
+
+METRIC = "GR decode-attn beam-rows/s + % bf16 MFMA peak (W=900), HBM GB/s (W=128)"
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+MALL_BYTES = 256 << 20
+PRIMARY = 2                   # Qwen3-0.6B shape, W=128
+SECONDARY = 4                 # Qwen3-0.6B shape, W=900
+KERNEL_SOURCES = ["shared_prefix_beam_amd/csrc/gr_attn_kernels.hip",
+                  "shared_prefix_beam_amd/csrc/gr_attn_api.cpp"]
+
+
+def algorithmic(inp: I.Inputs):
+    """(bytes, flops) the method must move / compute, each counted once.
+
+    bytes: ContextKV K+V of every (request, KV head) once, q and out once,
+    fp32 LSE, the BeamPath entries in use and every distinct BeamKV row a
+    path references (K+V).  flops: 4*W*Hq*D*L per request for the shared
+    stage (QK^T and PV); the beam stage and softmax are not counted.
+    """
+    wl = inp.wl
+    U = I.unique_beam_rows(inp)
+    nbytes = 0
+    flops = 0
+    for b in range(inp.B):
+        Wb = int(inp.row_offset[b + 1] - inp.row_offset[b])
+        L = int(inp.ctx_len[b])
+        T = int(inp.beam_len[b])
+        nbytes += 4 * L * wl.Hkv * wl.D + 4 * Wb * wl.Hq * wl.D + 4 * Wb * wl.Hq \
+            + 4 * Wb * T + 4 * U[b] * wl.Hkv * wl.D
+        flops += 4 * Wb * wl.Hq * wl.D * L
+    return nbytes, flops
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM traffic per launch from a committed rocprofv3 --pmc summary, if it
+    was taken from the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_fused_decode_attn_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_sha") != kernel_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def measure(cfg: int, steps: int, warmup: int):
+    import torch
+    from shared_prefix_beam_amd import gr_attn
+
+    inp = I.generate(I.WORKLOADS[cfg])
+    nbytes, flops = algorithmic(inp)
+    base = I.to_torch(inp)
+    footprint = sum(t.numel() * t.element_size() for t in base.values()) \
+        + base["q"].numel() * 2 + base["q"].shape[0] * base["q"].shape[1] * 4
+    n_sets = max(2, int(np.ceil(2 * MALL_BYTES / footprint)) + 1)
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(n_sets - 1)]
+    outs = [(torch.empty_like(s["q"]),
+             torch.empty(s["q"].shape[:2], dtype=torch.float32, device="cuda")) for s in sets]
+    W_max = int(max(inp.wl.W))
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        s = sets[i % n_sets]
+        o, l = outs[i % n_sets]
+        gr_attn.decode_attn(s["q"], s["ctx_k"], s["ctx_v"], s["ctx_len"], s["beam_k"],
+                            s["beam_v"], s["beam_path"], s["beam_len"], s["row_offset"],
+                            W_max=W_max, out=o, lse=l, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / steps
+
+    # per-launch durations with events on the launch stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    # spot check of a few rows against the oracle (not timed)
+    from oracle import oracle as O
+    rows = sorted({0, inp.R // 2, inp.R - 1})
+    out, lse = outs[0]
+    step(0)
+    torch.cuda.synchronize()
+    ref_o, ref_l = O.decode_attn_inputs(inp, rows=rows)
+    got_o = out.float().cpu().numpy()[rows]
+    spot = float(np.abs(got_o - ref_o).max())
+    spot_lse = float(np.abs(lse.cpu().numpy()[rows] - ref_l).max())
+
+    return dict(inp=inp, nbytes=nbytes, flops=flops, ms_per_step=ms_per_step,
+                launch_ms=launch_ms, n_sets=n_sets, spot_abs=spot, spot_lse=spot_lse)
+
+
+def cpu_baseline(inp: I.Inputs, max_rows: int):
+    from oracle import oracle as O
+    rows = np.arange(min(inp.R, max_rows))
+    n = O.default_threads()
+    t0 = time.perf_counter()
+    O.decode_attn_inputs(inp, rows=rows, n_threads=n)
+    dt = time.perf_counter() - t0
+    return {"value": len(rows) / dt, "unit": "beam-rows/s", "cores": n, "kind": "oracle",
+            "sample": f"fp64 oracle on {len(rows)} of {inp.R} rows (all {inp.wl.Hq} heads) "
+                      f"of the same workload, {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path "
+              "shards by request or KV head with no exchange, so run one process per GPU.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    prim = measure(PRIMARY, args.steps, args.warmup)
+    inp = prim["inp"]
+    t_launch = prim["launch_ms"] * 1e-3
+    achieved = prim["nbytes"] / t_launch / 1e9
+    traffic = recorded_traffic(inp.wl.name)
+    line = {
+        "metric": METRIC,
+        "value": inp.R / (prim["ms_per_step"] * 1e-3),
+        "unit": "beam-rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": prim["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": inp.wl.name, "B": inp.B, "beams_per_request": int(inp.wl.W[0]),
+                   "ctx_len": int(inp.ctx_len[0]), "beam_tokens": int(inp.beam_len[0]),
+                   "Hq": inp.wl.Hq, "Hkv": inp.wl.Hkv, "D": inp.wl.D, "rows": inp.R,
+                   "input_copies_rotated": prim["n_sets"]},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": "fused_decode_attn", "launch_us": prim["launch_ms"] * 1e3,
+                     "algorithmic_bytes": prim["nbytes"]},
+        "spot_check": {"max_abs": prim["spot_abs"], "lse_abs": prim["spot_lse"]},
+    }
+    if not args.no_secondary:
+        sec = measure(SECONDARY, args.steps, args.warmup)
+        si = sec["inp"]
+        tf = sec["flops"] / (sec["launch_ms"] * 1e-3) / 1e12
+        line["secondary"] = {
+            "workload": si.wl.name, "value": si.R / (sec["ms_per_step"] * 1e-3),
+            "unit": "beam-rows/s", "ms_per_step": sec["ms_per_step"],
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
+                         "traffic": recorded_traffic(si.wl.name),
+                         "launch_us": sec["launch_ms"] * 1e3, "algorithmic_flops": sec["flops"],
+                         "hbm_GBps": sec["nbytes"] / (sec["launch_ms"] * 1e-3) / 1e9},
+            "spot_check": {"max_abs": sec["spot_abs"], "lse_abs": sec["spot_lse"]},
+        }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(inp, max_rows=inp.R)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,134 @@
+/*
+ * gr_attn.h -- C ABI of the MI355X (gfx950) decode-attention library for
+ * large-beam generative recommendation.
+ *
+ * The operation (GR-Inference blog on developer.nvidia.cn, section on kernel
+ * design; xGR paper review on xllm-io, section "xAttention", three-stage
+ * computation; SID-GR Inference README, section "Design Highlights"):
+ *
+ *   Every request b owns one long ContextKV written at prefill and shared by
+ *   all of its W_b live beams, plus short per-beam BeamKV tokens reached
+ *   through a BeamPath index table.  For every packed query row r of request
+ *   b and every query head h (KV head g = h / (Hq/Hkv)), the library computes
+ *   softmax attention over the concatenation
+ *       ContextKV tokens 0 .. ctx_len[b]-1            (shared stage)
+ *    ++ BeamKV tokens beam_path[r][0 .. beam_len[b]-1]  (per-beam stage)
+ *   and combines the two parts by their log-sum-exp (merge stage):
+ *       out[r][h][:] = sum_j softmax_j(scale * q.K_j) V_j        (bf16)
+ *       lse[r][h]    = ln sum_j exp(scale * q.K_j)               (fp32)
+ *   A row with no key at all gets out = 0 and lse = -inf.
+ *
+ * Layouts (all row-major, contiguous; bf16 = raw 16-bit bfloat16):
+ *   q          bf16  [R][Hq][D]                 query rows of all requests, packed
+ *   ctx_k/v    bf16  [B][ctx_cap][Hkv][D]       dense ContextKV per request
+ *   ctx_len    int32 [B]                        0 <= ctx_len[b] <= ctx_cap
+ *   beam_k/v   bf16  [B][beam_cap][Hkv][D]      BeamKV pool per request
+ *   beam_path  int32 [R][T_cap]                 per-request BeamKV token indices
+ *   beam_len   int32 [B]                        0 <= beam_len[b] <= T_cap
+ *   row_offset int32 [B+1]                      request b owns rows
+ *                                               row_offset[b] .. row_offset[b+1]-1
+ *   out        bf16  [R][Hq][D]
+ *   lse        fp32  [R][Hq]                    natural log, scale included
+ *
+ * Ownership and threading: the caller owns every buffer (device memory,
+ * except the dims struct, which is host memory and is read during the call
+ * only).  A call only enqueues work on `stream` (a hipStream_t; NULL = the
+ * null stream) and returns; it never allocates, frees, copies between host
+ * and device, synchronises, or reads device memory from the host, so it may
+ * be captured into a HIP graph.  The library keeps no mutable global state:
+ * concurrent calls on different streams are safe as long as their out/lse
+ * buffers differ.  out and lse must not alias any input.
+ *
+ * Errors: every entry point returns GR_OK (0) or a negative GR_ERR_* code and
+ * then has enqueued nothing, except GR_ERR_LAUNCH, which reports a failed
+ * kernel launch.  Device-resident metadata (ctx_len, beam_len, row_offset,
+ * beam_path) is not read by the host: its bounds above are preconditions.
+ * gr_check_metadata() verifies them on the device when a caller cannot
+ * guarantee them.
+ */
+#ifndef GR_ATTN_H
+#define GR_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    GR_OK = 0,
+    GR_ERR_NULL = -1,        /* a required pointer is NULL */
+    GR_ERR_DIMS = -2,        /* inconsistent sizes (Hq % Hkv, R < 0, scale < 0, ...) */
+    GR_ERR_UNSUPPORTED = -3, /* D not 64/128, G > 8, no gfx950 device, ... */
+    GR_ERR_ALIGN = -4,       /* a bf16 tensor pointer is not 16-byte aligned */
+    GR_ERR_LAUNCH = -5,      /* the HIP runtime rejected a kernel launch */
+    GR_ERR_DEVICE = -6       /* a HIP runtime query failed */
+};
+
+/* Sizes of one call.  Host memory; read only during the call. */
+typedef struct gr_decode_attn_dims {
+    int32_t B;        /* requests (>= 0) */
+    int32_t R;        /* packed query rows = row_offset[B] (>= 0) */
+    int32_t Hq;       /* query heads */
+    int32_t Hkv;      /* KV heads; Hq % Hkv == 0 and G = Hq / Hkv <= 8 */
+    int32_t D;        /* head dim: 64 or 128 */
+    int32_t W_max;    /* upper bound on any request's row count W_b (>= 0) */
+    int32_t T_cap;    /* row stride of beam_path; upper bound on beam_len[b] */
+    int32_t reserved; /* must be 0 */
+    int64_t ctx_cap;  /* ContextKV tokens per request in ctx_k / ctx_v */
+    int64_t beam_cap; /* BeamKV tokens per request in beam_k / beam_v */
+    float scale;      /* softmax scale applied to q.k; 0 selects 1/sqrt(D) */
+    int32_t flags;    /* must be 0 */
+} gr_decode_attn_dims;
+
+/*
+ * Large-beam decode attention (shared ContextKV stage on bf16 MFMA with an
+ * online softmax, per-beam BeamPath gather, log-sum-exp merge), one launch
+ * on `stream`.  row_offset is a DEVICE pointer to int32[B+1].
+ * The ContextKV of each (request, KV head) is read from HBM once per call
+ * rather than once per beam.
+ */
+int gr_decode_attn(const gr_decode_attn_dims *dims, const int32_t *row_offset,
+                   const void *q, const void *ctx_k, const void *ctx_v,
+                   const int32_t *ctx_len, const void *beam_k, const void *beam_v,
+                   const int32_t *beam_path, const int32_t *beam_len, void *out,
+                   float *lse, void *stream);
+
+/*
+ * The same operation computed the way a generic decode-attention kernel
+ * does it: every (row, head) independently reads its request's whole
+ * ContextKV (SID-GR README, section "Performance Breakdown": the
+ * general path treats B x W beams as independent decode rows).  Same
+ * arguments, layouts and results; kept as an in-library comparator.
+ * Requires ctx_cap + T_cap <= 16384.
+ */
+int gr_decode_attn_generic(const gr_decode_attn_dims *dims, const int32_t *row_offset,
+                           const void *q, const void *ctx_k, const void *ctx_v,
+                           const int32_t *ctx_len, const void *beam_k, const void *beam_v,
+                           const int32_t *beam_path, const int32_t *beam_len, void *out,
+                           float *lse, void *stream);
+
+/*
+ * Device-side check of the metadata preconditions above: row_offset is
+ * non-decreasing with row_offset[0] = 0, row_offset[B] = R and every
+ * W_b <= W_max; every ctx_len[b] in [0, ctx_cap]; every beam_len[b] in
+ * [0, T_cap]; every used beam_path entry in [0, beam_cap).  Writes the number
+ * of violations (0 = valid) to the DEVICE int32 *violations; enqueued on
+ * `stream` like the other calls.
+ */
+int gr_check_metadata(const gr_decode_attn_dims *dims, const int32_t *row_offset,
+                      const int32_t *ctx_len, const int32_t *beam_path,
+                      const int32_t *beam_len, int32_t *violations, void *stream);
+
+/* Static description of a status code. */
+const char *gr_status_str(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int gr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GR_ATTN_H */

@@ -34,6 +34,15 @@ def build(force: bool = False) -> str:
     return _LIB
 
 
+def default_threads() -> int:
+    """Host threads for the oracle: the CPUs this process may run on, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
 def _open(path: str):
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
@@ -109,7 +118,7 @@ def _call(lib, q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path, beam_len, ro
     out = np.zeros((n, Hq, D), dtype=np.float64)
     lse = np.zeros((n, Hq), dtype=np.float64)
     if n_threads is None:
-        n_threads = os.cpu_count() or 1
+        n_threads = default_threads()
     st = lib.oracle_decode_attn(B, R, Hq, Hkv, D, T_cap, ctx_cap, beam_cap, float(scale),
                                 _ptr(q), _ptr(ctx_k), _ptr(ctx_v), _ptr(ctx_len), _ptr(beam_k),
                                 _ptr(beam_v), _ptr(beam_path), _ptr(beam_len), _ptr(row_offset),

@@ -1,0 +1,259 @@
+// Host side of the C ABI declared in include/gr_attn.h: argument validation,
+// the work decomposition of the fused kernel, and launches on the caller's
+// stream.  Nothing here allocates, synchronises or reads device memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "gr_attn.h"
+#include "gr_attn_internal.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// gfx950 check, cached per device ordinal (the only global state: immutable
+// after first use).
+int device_ok()
+{
+    static std::once_flag once;
+    static int ok_mask[64];
+    static int ndev = 0;
+    std::call_once(once, [] {
+        if (hipGetDeviceCount(&ndev) != hipSuccess)
+            ndev = 0;
+        if (ndev > 64)
+            ndev = 64;
+        for (int d = 0; d < ndev; ++d) {
+            hipDeviceProp_t prop;
+            ok_mask[d] = hipGetDeviceProperties(&prop, d) == hipSuccess &&
+                         std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        }
+    });
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= ndev)
+        return GR_ERR_DEVICE;
+    return ok_mask[dev] ? GR_OK : GR_ERR_UNSUPPORTED;
+}
+
+int validate(const gr_decode_attn_dims *d)
+{
+    if (!d)
+        return GR_ERR_NULL;
+    if (d->B < 0 || d->R < 0 || d->Hq <= 0 || d->Hkv <= 0 || d->W_max < 0 || d->T_cap < 0 ||
+        d->ctx_cap < 0 || d->beam_cap < 0 || d->reserved != 0 || d->flags != 0)
+        return GR_ERR_DIMS;
+    if (d->Hq % d->Hkv != 0)
+        return GR_ERR_DIMS;
+    if (!(d->scale >= 0.f) || std::isinf(d->scale))
+        return GR_ERR_DIMS;
+    if (d->D != 64 && d->D != 128)
+        return GR_ERR_UNSUPPORTED;
+    if (d->Hq / d->Hkv > 8)
+        return GR_ERR_UNSUPPORTED;
+    // index arithmetic of the kernels is 32-bit per request token index
+    if (d->ctx_cap > INT32_MAX || d->beam_cap > INT32_MAX ||
+        static_cast<int64_t>(d->W_max) * (d->Hq / d->Hkv) > INT32_MAX)
+        return GR_ERR_DIMS;
+    return GR_OK;
+}
+
+int validate_buffers(const gr_decode_attn_dims *d, const int32_t *row_offset, const void *q,
+                     const void *ctx_k, const void *ctx_v, const int32_t *ctx_len,
+                     const void *beam_k, const void *beam_v, const int32_t *beam_path,
+                     const int32_t *beam_len, const void *out, const float *lse)
+{
+    if (d->B > 0 && (!row_offset || !ctx_len || !beam_len || !ctx_k || !ctx_v || !beam_k ||
+                     !beam_v))
+        return GR_ERR_NULL;
+    if (d->R > 0 && (!q || !out || !lse || (!beam_path && d->T_cap > 0)))
+        return GR_ERR_NULL;
+    const void *bf[] = {q, ctx_k, ctx_v, beam_k, beam_v, out};
+    for (const void *p : bf)
+        if (p && !aligned16(p))
+            return GR_ERR_ALIGN;
+    if ((lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) ||
+        (beam_path && (reinterpret_cast<uintptr_t>(beam_path) & 3u)))
+        return GR_ERR_ALIGN;
+    return GR_OK;
+}
+
+gr::Params make_params(const gr_decode_attn_dims *d, const int32_t *row_offset, const void *q,
+                       const void *ctx_k, const void *ctx_v, const int32_t *ctx_len,
+                       const void *beam_k, const void *beam_v, const int32_t *beam_path,
+                       const int32_t *beam_len, void *out, float *lse)
+{
+    gr::Params p{};
+    p.q = static_cast<const uint16_t *>(q);
+    p.ctx_k = static_cast<const uint16_t *>(ctx_k);
+    p.ctx_v = static_cast<const uint16_t *>(ctx_v);
+    p.beam_k = static_cast<const uint16_t *>(beam_k);
+    p.beam_v = static_cast<const uint16_t *>(beam_v);
+    p.ctx_len = ctx_len;
+    p.beam_len = beam_len;
+    p.beam_path = beam_path;
+    p.row_offset = row_offset;
+    p.out = static_cast<uint16_t *>(out);
+    p.lse = lse;
+    p.B = d->B;
+    p.R = d->R;
+    p.Hq = d->Hq;
+    p.Hkv = d->Hkv;
+    p.G = d->Hq / d->Hkv;
+    p.D = d->D;
+    p.T_cap = d->T_cap;
+    p.ctx_cap = d->ctx_cap;
+    p.beam_cap = d->beam_cap;
+    const double scale = d->scale > 0.f ? d->scale : 1.0 / std::sqrt((double)d->D);
+    p.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
+    return p;
+}
+
+// Work decomposition.  A workgroup covers 64*NQT stacked query rows of one
+// (request, KV head) pair and splits that pair's context over NKS key
+// streams.  Large stacks take wide query tiles (the K/V tile in LDS then
+// serves 4 waves); small stacks take narrow tiles and more key streams so
+// that the grid still covers every compute unit.
+struct Plan {
+    int nqt, nks, n_qt, grid;
+};
+
+constexpr int kCUs = 256;
+
+Plan plan(const gr_decode_attn_dims *d)
+{
+    const int G = d->Hq / d->Hkv;
+    const int64_t M = static_cast<int64_t>(d->W_max) * G;
+    const int pairs = d->B * d->Hkv;
+    static const int cand[][2] = {{4, 1}, {2, 2}, {1, 4}};
+    Plan best{1, 4, 0, 0};
+    const char *env = std::getenv("GR_ATTN_TILE");     // "NQT,NKS", tuning only
+    int fq = 0, fk = 0;
+    if (env && std::sscanf(env, "%d,%d", &fq, &fk) == 2 && gr::fused_lds_bytes(d->D, fq, fk) > 0) {
+        best.nqt = fq;
+        best.nks = fk;
+    } else {
+        for (const auto &c : cand) {
+            const int64_t n_qt = (M + 64 * c[0] - 1) / (64 * c[0]);
+            if (pairs * n_qt >= kCUs || (c[0] == 1)) {
+                best.nqt = c[0];
+                best.nks = c[1];
+                break;
+            }
+        }
+    }
+    best.n_qt = static_cast<int>((M + 64 * best.nqt - 1) / (64 * best.nqt));
+    const int pairs_per_xcd = (pairs + 7) / 8;
+    best.grid = 8 * pairs_per_xcd * best.n_qt;
+    return best;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gr_decode_attn(const gr_decode_attn_dims *d, const int32_t *row_offset, const void *q,
+                   const void *ctx_k, const void *ctx_v, const int32_t *ctx_len,
+                   const void *beam_k, const void *beam_v, const int32_t *beam_path,
+                   const int32_t *beam_len, void *out, float *lse, void *stream)
+{
+    int st = validate(d);
+    if (st != GR_OK)
+        return st;
+    st = validate_buffers(d, row_offset, q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path,
+                          beam_len, out, lse);
+    if (st != GR_OK)
+        return st;
+    if (d->R == 0 || d->B == 0 || d->W_max == 0)
+        return GR_OK;
+    st = device_ok();
+    if (st != GR_OK)
+        return st;
+    gr::Params p = make_params(d, row_offset, q, ctx_k, ctx_v, ctx_len, beam_k, beam_v,
+                               beam_path, beam_len, out, lse);
+    const Plan pl = plan(d);
+    p.n_qt = pl.n_qt;
+    if (pl.grid <= 0)
+        return GR_OK;
+    const hipError_t e =
+        gr::launch_fused(p, pl.nqt, pl.nks, pl.grid, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GR_OK : GR_ERR_LAUNCH;
+}
+
+int gr_decode_attn_generic(const gr_decode_attn_dims *d, const int32_t *row_offset,
+                           const void *q, const void *ctx_k, const void *ctx_v,
+                           const int32_t *ctx_len, const void *beam_k, const void *beam_v,
+                           const int32_t *beam_path, const int32_t *beam_len, void *out,
+                           float *lse, void *stream)
+{
+    int st = validate(d);
+    if (st != GR_OK)
+        return st;
+    st = validate_buffers(d, row_offset, q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path,
+                          beam_len, out, lse);
+    if (st != GR_OK)
+        return st;
+    if (d->ctx_cap + d->T_cap > gr::GENERIC_MAX_KEYS)
+        return GR_ERR_UNSUPPORTED;
+    if (d->R == 0 || d->B == 0)
+        return GR_OK;
+    st = device_ok();
+    if (st != GR_OK)
+        return st;
+    const gr::Params p = make_params(d, row_offset, q, ctx_k, ctx_v, ctx_len, beam_k, beam_v,
+                                     beam_path, beam_len, out, lse);
+    const hipError_t e = gr::launch_generic(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GR_OK : GR_ERR_LAUNCH;
+}
+
+int gr_check_metadata(const gr_decode_attn_dims *d, const int32_t *row_offset,
+                      const int32_t *ctx_len, const int32_t *beam_path,
+                      const int32_t *beam_len, int32_t *violations, void *stream)
+{
+    int st = validate(d);
+    if (st != GR_OK)
+        return st;
+    if (!violations || (d->B > 0 && (!row_offset || !ctx_len || !beam_len)) ||
+        (d->R > 0 && d->T_cap > 0 && !beam_path))
+        return GR_ERR_NULL;
+    st = device_ok();
+    if (st != GR_OK)
+        return st;
+    gr::MetaCheck c{};
+    c.row_offset = row_offset;
+    c.ctx_len = ctx_len;
+    c.beam_len = beam_len;
+    c.beam_path = beam_path;
+    c.violations = violations;
+    c.B = d->B;
+    c.R = d->R;
+    c.W_max = d->W_max;
+    c.T_cap = d->T_cap;
+    c.ctx_cap = d->ctx_cap;
+    c.beam_cap = d->beam_cap;
+    const hipError_t e = gr::launch_check(c, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GR_OK : GR_ERR_LAUNCH;
+}
+
+const char *gr_status_str(int status)
+{
+    switch (status) {
+    case GR_OK: return "ok";
+    case GR_ERR_NULL: return "a required pointer is NULL";
+    case GR_ERR_DIMS: return "inconsistent or out-of-range dimensions";
+    case GR_ERR_UNSUPPORTED: return "unsupported configuration or device";
+    case GR_ERR_ALIGN: return "misaligned tensor pointer";
+    case GR_ERR_LAUNCH: return "kernel launch failed";
+    case GR_ERR_DEVICE: return "HIP device query failed";
+    default: return "unknown status";
+    }
+}
+
+int gr_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,41 @@
+// Internal interface between the host-side API and the device code.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gr {
+
+// Everything a kernel needs about one call (passed by value).
+struct Params {
+    const uint16_t *q, *ctx_k, *ctx_v, *beam_k, *beam_v;
+    const int32_t *ctx_len, *beam_len, *beam_path, *row_offset;
+    uint16_t *out;
+    float *lse;
+    int B, R, Hq, Hkv, G, D, T_cap;
+    int64_t ctx_cap, beam_cap;
+    float scale_log2;   // softmax scale * log2(e)
+    int n_qt;           // query tiles per (request, KV head) pair in the fused grid
+};
+
+struct MetaCheck {
+    const int32_t *row_offset, *ctx_len, *beam_len, *beam_path;
+    int32_t *violations;
+    int B, R, W_max, T_cap;
+    int64_t ctx_cap, beam_cap;
+};
+
+// Longest key list the generic comparator keeps in LDS.
+constexpr int GENERIC_MAX_KEYS = 16320;
+
+// Fused-kernel instantiations: (head dim, query waves per stream NQT, key
+// streams NKS).  A workgroup has NQT*NKS waves and covers 64*NQT query rows.
+#define GR_FOR_EACH_FUSED_CONFIG(X) \
+    X(128, 1, 4) X(128, 2, 2) X(128, 4, 2) X(128, 4, 1) X(128, 2, 1) X(128, 1, 2) \
+    X(64, 1, 4) X(64, 2, 2) X(64, 4, 2) X(64, 4, 1) X(64, 2, 1) X(64, 1, 2)
+
+int fused_lds_bytes(int D, int nqt, int nks);
+hipError_t launch_fused(const Params &p, int nqt, int nks, int grid, hipStream_t s);
+hipError_t launch_generic(const Params &p, hipStream_t s);
+hipError_t launch_check(const MetaCheck &c, hipStream_t s);
+
+}  // namespace gr

@@ -1,0 +1,201 @@
+"""Python binding of the C ABI in include/gr_attn.h (ctypes).
+
+Argument marshalling only: torch tensors supply device pointers and the
+current HIP stream; every step of the computation runs in libgr_attn.so.
+Loading fails loudly when the library has not been built.
+
+Functions with the C names take the same arguments as the C entry points
+(a ``Dims`` struct plus raw pointers); ``decode_attn`` / ``decode_attn_generic``
+/ ``check_metadata`` accept torch tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgr_attn.so")
+
+GR_OK = 0
+GR_ERR_NULL = -1
+GR_ERR_DIMS = -2
+GR_ERR_UNSUPPORTED = -3
+GR_ERR_ALIGN = -4
+GR_ERR_LAUNCH = -5
+GR_ERR_DEVICE = -6
+
+EXPORTS = ("gr_decode_attn", "gr_decode_attn_generic", "gr_check_metadata",
+           "gr_status_str", "gr_version")
+
+
+class Dims(ctypes.Structure):
+    """``gr_decode_attn_dims`` (host memory)."""
+
+    _fields_ = [("B", ctypes.c_int32), ("R", ctypes.c_int32), ("Hq", ctypes.c_int32),
+                ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32), ("W_max", ctypes.c_int32),
+                ("T_cap", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("ctx_cap", ctypes.c_int64), ("beam_cap", ctypes.c_int64),
+                ("scale", ctypes.c_float), ("flags", ctypes.c_int32)]
+
+
+class GrAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: status {status} ({gr_status_str(status)})")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libgr_attn.so; raise if it is missing (no fallback path exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run "
+                              "`python -m shared_prefix_beam_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        DP = ctypes.POINTER(Dims)
+        attn_args = [DP, P, P, P, P, P, P, P, P, P, P, P, P]
+        for name in ("gr_decode_attn", "gr_decode_attn_generic"):
+            fn = getattr(lib, name)
+            fn.argtypes = attn_args
+            fn.restype = ctypes.c_int
+        lib.gr_check_metadata.argtypes = [DP, P, P, P, P, P, P]
+        lib.gr_check_metadata.restype = ctypes.c_int
+        lib.gr_status_str.argtypes = [ctypes.c_int]
+        lib.gr_status_str.restype = ctypes.c_char_p
+        lib.gr_version.argtypes = []
+        lib.gr_version.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+# ---- the C entry points, same names and arguments -------------------------
+def gr_decode_attn(dims: Dims, row_offset, q, ctx_k, ctx_v, ctx_len, beam_k, beam_v,
+                   beam_path, beam_len, out, lse, stream) -> int:
+    return load().gr_decode_attn(ctypes.byref(dims), row_offset, q, ctx_k, ctx_v, ctx_len,
+                                 beam_k, beam_v, beam_path, beam_len, out, lse, stream)
+
+
+def gr_decode_attn_generic(dims: Dims, row_offset, q, ctx_k, ctx_v, ctx_len, beam_k, beam_v,
+                           beam_path, beam_len, out, lse, stream) -> int:
+    return load().gr_decode_attn_generic(ctypes.byref(dims), row_offset, q, ctx_k, ctx_v,
+                                         ctx_len, beam_k, beam_v, beam_path, beam_len, out,
+                                         lse, stream)
+
+
+def gr_check_metadata(dims: Dims, row_offset, ctx_len, beam_path, beam_len, violations,
+                      stream) -> int:
+    return load().gr_check_metadata(ctypes.byref(dims), row_offset, ctx_len, beam_path,
+                                    beam_len, violations, stream)
+
+
+def gr_status_str(status: int) -> str:
+    return load().gr_status_str(int(status)).decode()
+
+
+def gr_version() -> int:
+    return load().gr_version()
+
+
+# ---- torch front end -------------------------------------------------------
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream or None
+
+
+def make_dims(q, ctx_k, beam_k, beam_path, W_max: int, scale: Optional[float] = None) -> Dims:
+    R, Hq, D = q.shape
+    B, ctx_cap, Hkv, _ = ctx_k.shape
+    return Dims(B=B, R=R, Hq=Hq, Hkv=Hkv, D=D, W_max=int(W_max), T_cap=beam_path.shape[1],
+                reserved=0, ctx_cap=ctx_cap, beam_cap=beam_k.shape[1],
+                scale=0.0 if scale is None else float(scale), flags=0)
+
+
+def _check(q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path, beam_len, row_offset):
+    import torch
+    for name, t, dt in (("q", q, torch.bfloat16), ("ctx_k", ctx_k, torch.bfloat16),
+                        ("ctx_v", ctx_v, torch.bfloat16), ("beam_k", beam_k, torch.bfloat16),
+                        ("beam_v", beam_v, torch.bfloat16), ("ctx_len", ctx_len, torch.int32),
+                        ("beam_len", beam_len, torch.int32),
+                        ("beam_path", beam_path, torch.int32),
+                        ("row_offset", row_offset, torch.int32)):
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dim() != 3 or ctx_k.dim() != 4 or beam_k.dim() != 4 or beam_path.dim() != 2:
+        raise ValueError("bad tensor ranks")
+    if ctx_v.shape != ctx_k.shape or beam_v.shape != beam_k.shape:
+        raise ValueError("K and V shapes differ")
+    B = ctx_k.shape[0]
+    if beam_k.shape[0] != B or ctx_len.numel() != B or beam_len.numel() != B \
+            or row_offset.numel() != B + 1 or beam_path.shape[0] != q.shape[0]:
+        raise ValueError("request count mismatch")
+    if ctx_k.shape[2:] != beam_k.shape[2:] or ctx_k.shape[3] != q.shape[2]:
+        raise ValueError("head layout mismatch")
+
+
+def _run(fn_name, q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path, beam_len, row_offset,
+         W_max, scale, out, lse, stream) -> Tuple:
+    import torch
+    _check(q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path, beam_len, row_offset)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    dims = make_dims(q, ctx_k, beam_k, beam_path, W_max, scale)
+    fn = gr_decode_attn if fn_name == "fused" else gr_decode_attn_generic
+    st = fn(dims, _ptr(row_offset), _ptr(q), _ptr(ctx_k), _ptr(ctx_v), _ptr(ctx_len),
+            _ptr(beam_k), _ptr(beam_v), _ptr(beam_path), _ptr(beam_len), _ptr(out), _ptr(lse),
+            _stream_handle(stream))
+    if st != GR_OK:
+        raise GrAttnError(st, "gr_decode_attn" if fn_name == "fused" else
+                          "gr_decode_attn_generic")
+    return out, lse
+
+
+def decode_attn(q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path, beam_len, row_offset,
+                W_max: int, scale: Optional[float] = None, out=None, lse=None, stream=None):
+    """Fused shared-context / BeamPath / LSE-merge decode attention.
+
+    Tensors as in include/gr_attn.h (bf16 / int32, contiguous, on the GPU).
+    ``W_max`` bounds every request's row count.  Returns (out bf16 [R,Hq,D],
+    lse fp32 [R,Hq]); enqueued on ``stream`` (default: torch's current one).
+    """
+    return _run("fused", q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path, beam_len,
+                row_offset, W_max, scale, out, lse, stream)
+
+
+def decode_attn_generic(q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path, beam_len,
+                        row_offset, W_max: int, scale: Optional[float] = None, out=None,
+                        lse=None, stream=None):
+    """Same result through the generic per-row comparator kernel."""
+    return _run("generic", q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path, beam_len,
+                row_offset, W_max, scale, out, lse, stream)
+
+
+def check_metadata(ctx_len, beam_path, beam_len, row_offset, *, B, R, Hq, Hkv, D, W_max,
+                   ctx_cap, beam_cap, violations=None, stream=None):
+    """Device-side precondition check; returns the int32 violation count tensor."""
+    import torch
+    if violations is None:
+        violations = torch.zeros(1, dtype=torch.int32, device=row_offset.device)
+    dims = Dims(B=B, R=R, Hq=Hq, Hkv=Hkv, D=D, W_max=W_max, T_cap=beam_path.shape[1],
+                reserved=0, ctx_cap=ctx_cap, beam_cap=beam_cap, scale=0.0, flags=0)
+    st = gr_check_metadata(dims, _ptr(row_offset), _ptr(ctx_len), _ptr(beam_path),
+                           _ptr(beam_len), _ptr(violations), _stream_handle(stream))
+    if st != GR_OK:
+        raise GrAttnError(st, "gr_check_metadata")
+    return violations

@@ -283,3 +283,21 @@ def unique_beam_rows(inp: Inputs) -> List[int]:
         T = int(inp.beam_len[b])
         out.append(int(np.unique(inp.beam_path[r0:r1, :T]).size) if T > 0 else 0)
     return out
+
+
+def to_torch(inp: Inputs, device="cuda"):
+    """Copy the generated buffers to ``device`` as torch tensors (bf16 / int32).
+
+    Returns a dict with the entry-point argument names.
+    """
+    import torch
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+    return dict(q=bf(inp.q), ctx_k=bf(inp.ctx_k), ctx_v=bf(inp.ctx_v), ctx_len=i32(inp.ctx_len),
+                beam_k=bf(inp.beam_k), beam_v=bf(inp.beam_v), beam_path=i32(inp.beam_path),
+                beam_len=i32(inp.beam_len), row_offset=i32(inp.row_offset))

@@ -1,0 +1,98 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol and
+rejects bad arguments in host validation, before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from shared_prefix_beam_amd import gr_attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gr_attn.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gr_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gr_attn.load()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == set(gr_attn.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_dims_struct_layout():
+    # int32 x8, int64 x2, float, int32 -> 56 bytes, int64 fields 8-aligned
+    assert ctypes.sizeof(gr_attn.Dims) == 56
+    assert gr_attn.Dims.ctx_cap.offset == 32 and gr_attn.Dims.scale.offset == 48
+
+
+def test_version_and_status_strings(lib):
+    assert gr_attn.gr_version() >= 100
+    assert gr_attn.gr_status_str(0) == "ok"
+    for code in (-1, -2, -3, -4, -5, -6):
+        assert gr_attn.gr_status_str(code) != "unknown status"
+
+
+def good_dims(**over):
+    d = dict(B=2, R=10, Hq=16, Hkv=8, D=128, W_max=5, T_cap=3, reserved=0, ctx_cap=64,
+             beam_cap=16, scale=0.0, flags=0)
+    d.update(over)
+    return gr_attn.Dims(**d)
+
+
+P16 = 0x10000        # fake, aligned, never dereferenced: validation fails first
+
+
+def call(dims, **ptrs):
+    args = dict(row_offset=P16, q=P16, ctx_k=P16, ctx_v=P16, ctx_len=P16, beam_k=P16,
+                beam_v=P16, beam_path=P16, beam_len=P16, out=P16, lse=P16)
+    args.update(ptrs)
+    return gr_attn.gr_decode_attn(dims, args["row_offset"], args["q"], args["ctx_k"],
+                                  args["ctx_v"], args["ctx_len"], args["beam_k"],
+                                  args["beam_v"], args["beam_path"], args["beam_len"],
+                                  args["out"], args["lse"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(Hq=12, Hkv=8), gr_attn.GR_ERR_DIMS),
+    (dict(R=-1), gr_attn.GR_ERR_DIMS),
+    (dict(B=-1), gr_attn.GR_ERR_DIMS),
+    (dict(scale=-1.0), gr_attn.GR_ERR_DIMS),
+    (dict(scale=float("nan")), gr_attn.GR_ERR_DIMS),
+    (dict(reserved=1), gr_attn.GR_ERR_DIMS),
+    (dict(flags=2), gr_attn.GR_ERR_DIMS),
+    (dict(D=96), gr_attn.GR_ERR_UNSUPPORTED),
+    (dict(Hq=32, Hkv=2), gr_attn.GR_ERR_UNSUPPORTED),
+])
+def test_bad_dims_rejected(over, code):
+    assert call(good_dims(**over)) == code
+
+
+def test_null_and_alignment_rejected():
+    assert gr_attn.load().gr_decode_attn(None, *([P16] * 11), None) == gr_attn.GR_ERR_NULL
+    assert call(good_dims(), q=None) == gr_attn.GR_ERR_NULL
+    assert call(good_dims(), row_offset=None) == gr_attn.GR_ERR_NULL
+    assert call(good_dims(), ctx_k=P16 + 8) == gr_attn.GR_ERR_ALIGN
+    assert call(good_dims(), out=P16 + 2) == gr_attn.GR_ERR_ALIGN
+    assert call(good_dims(), lse=P16 + 2) == gr_attn.GR_ERR_ALIGN
+
+
+def test_empty_call_is_a_no_op():
+    # nothing to compute: returns before any device access
+    assert call(good_dims(R=0, W_max=0)) == gr_attn.GR_OK
+
+
+def test_generic_rejects_too_long_context():
+    d = good_dims(ctx_cap=20000)
+    st = gr_attn.gr_decode_attn_generic(d, *([P16] * 11), None)
+    assert st == gr_attn.GR_ERR_UNSUPPORTED

@@ -1,0 +1,95 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerances: max abs 2e-2 and row-wise max rel 1e-2 on bf16 outputs, 1e-3 abs
+on fp32 LSE.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+from gpu_util import assert_parity, log, run_lib, sample_rows
+from oracle import oracle as O
+from shared_prefix_beam_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+_cache = {}
+
+
+def workload(cfg):
+    if cfg not in _cache:
+        _cache[cfg] = I.generate(I.WORKLOADS[cfg])
+    return _cache[cfg]
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("which", ["fused", "generic"])
+def test_workload_parity(cfg, which):
+    """Full-size workloads; the oracle evaluates a sample of rows (all rows
+    for the tiny workload) including every tile edge."""
+    inp = workload(cfg)
+    log(f"[parity] workload {cfg} ({inp.wl.name}) path={which} R={inp.R}")
+    out, lse = run_lib(inp, which)
+    rows = list(range(inp.R)) if cfg == 1 else sample_rows(inp, 192, seed=cfg)
+    ref_out, ref_lse = O.decode_attn_inputs(inp, rows=rows)
+    assert np.isfinite(out).all(), "NaN/inf anywhere in the output"
+    assert_parity(out[rows], lse[rows], ref_out, ref_lse, f"cfg{cfg}/{which}")
+
+
+SMALL = [
+    # (name, B, Hq, Hkv, D, W, ctx_len, beam_len, kwargs)
+    ("ragged_tails", 3, 16, 8, 128, [37, 5, 70], [1000, 33, 517], [3, 1, 5], {}),
+    ("g4_growing", 2, 32, 8, 128, [20, 45], [700, 1300], [5, 4], dict(grow_steps=True)),
+    ("d64_g2", 2, 4, 2, 64, [9, 40], [95, 300], [2, 3], {}),
+    ("mha_g1", 2, 8, 8, 128, [33, 64], [129, 64], [2, 2], {}),
+    ("g8", 1, 8, 1, 128, [24], [250], [3], {}),
+    ("one_beam", 2, 16, 8, 128, [1, 1], [513, 2], [3, 1], {}),
+    ("ctx_len_1", 2, 16, 8, 128, [4, 7], [1, 1], [2, 3], {}),
+    ("no_beam_tokens", 2, 16, 8, 128, [6, 3], [300, 77], [0, 0], dict(T_cap=3)),
+    ("no_context", 2, 16, 8, 128, [6, 3], [0, 0], [3, 2], dict(ctx_cap=64)),
+    ("empty_request", 3, 16, 8, 128, [5, 0, 4], [64, 50, 0], [2, 2, 0], dict(ctx_cap=64)),
+    ("no_keys_at_all", 1, 16, 8, 128, [3], [0], [0], dict(ctx_cap=32, T_cap=2)),
+    ("dup_paths", 2, 16, 8, 128, [60, 40], [256, 130], [3, 3], dict(dup_frac=0.3)),
+    ("sharp_q8", 2, 16, 8, 128, [30, 20], [900, 400], [3, 4], dict(q_std=8.0)),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+@pytest.mark.parametrize("which", ["fused", "generic"])
+def test_small_shapes_all_rows(case, which):
+    name, B, Hq, Hkv, D, W, L, T, kw = case
+    inp = I.custom(B=B, Hq=Hq, Hkv=Hkv, D=D, W=W, ctx_len=L, beam_len=T, seed=zlib.crc32(name.encode()) % 1000,
+                   **kw)
+    log(f"[parity] {name} path={which} R={inp.R} L={L} T={T}")
+    out, lse = run_lib(inp, which)
+    ref_out, ref_lse = O.decode_attn_inputs(inp)
+    assert_parity(out, lse, ref_out, ref_lse, f"{name}/{which}")
+
+
+def test_rising_scores_take_exact_sweep():
+    """Scores that grow by far more than 44 nats along the context: the
+    fixed first-tile reference would overflow, so the exact sweep must run."""
+    inp = I.custom(B=1, Hq=16, Hkv=8, D=128, W=[40], ctx_len=[600], beam_len=[2], seed=9)
+    k = I.bf16_bits_to_f32(inp.ctx_k).copy()
+    ramp = np.linspace(0.05, 6.0, inp.ctx_cap, dtype=np.float32)[None, :, None, None]
+    k = k * ramp
+    q = I.bf16_bits_to_f32(inp.q) * np.float32(4.0)
+    inp.ctx_k[:] = I.to_bf16_bits(k)
+    inp.q[:] = I.to_bf16_bits(q)
+    log("[parity] rising scores (exact re-sweep)")
+    out, lse = run_lib(inp)
+    ref_out, ref_lse = O.decode_attn_inputs(inp)
+    assert (ref_lse > 60).any()
+    assert_parity(out, lse, ref_out, ref_lse, "rising")
+
+
+def test_explicit_scale():
+    inp = I.custom(B=2, Hq=16, Hkv=8, D=128, W=[10, 7], ctx_len=[200, 90], beam_len=[3, 2],
+                   seed=17)
+    log("[parity] explicit scale 0.05")
+    out, lse = run_lib(inp, scale=0.05)
+    ref_out, ref_lse = O.decode_attn(
+        inp.q, inp.ctx_k, inp.ctx_v, inp.ctx_len, inp.beam_k, inp.beam_v, inp.beam_path,
+        inp.beam_len, inp.row_offset, scale=0.05)
+    assert_parity(out, lse, ref_out, ref_lse, "scale0.05")
