@@ -158,6 +158,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--only-secondary", action="store_true",
+                    help="measure only the 900-beam workload (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path "
@@ -170,6 +172,11 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
 
+    if args.only_secondary:
+        sec = measure(SECONDARY, args.steps, args.warmup)
+        print(json.dumps({"workload": sec["inp"].wl.name, "launch_us": sec["launch_ms"] * 1e3,
+                          "ms_per_step": sec["ms_per_step"]}), flush=True)
+        return
     prim = measure(PRIMARY, args.steps, args.warmup)
     inp = prim["inp"]
     t_launch = prim["launch_ms"] * 1e-3

@@ -32,8 +32,9 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 target feature: harmless
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    noise = ("is not a recognized feature for this target", "reserved registers", "^   ", "^      |")
+    err = "\n".join(l for l in res.stderr.splitlines()
+                     if not any(n.strip("^") in l for n in noise))
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():

@@ -114,23 +114,24 @@ gr::Params make_params(const gr_decode_attn_dims *d, const int32_t *row_offset, 
     return p;
 }
 
-// Work decomposition.  A workgroup covers 64*NQT stacked query rows of one
-// (request, KV head) pair and splits that pair's context over NKS key
-// streams.  Large stacks take wide query tiles (the K/V tile in LDS then
-// serves 4 waves); small stacks take narrow tiles and more key streams so
-// that the grid still covers every compute unit.
+// Work decomposition.  A workgroup covers 32*NQT stacked query rows of one
+// (request, KV head) pair (a wave owns 32 rows) and splits that pair's
+// context over NKS key streams.  Wide query tiles share each K/V tile in LDS
+// between more waves; more key streams keep the grid large when the stacks
+// are short.  The first candidate that puts at least two waves on every
+// SIMD is taken.
 struct Plan {
     int nqt, nks, n_qt, grid;
 };
 
-constexpr int kCUs = 256;
+constexpr int kSIMDs = 256 * 4;
 
 Plan plan(const gr_decode_attn_dims *d)
 {
     const int G = d->Hq / d->Hkv;
     const int64_t M = static_cast<int64_t>(d->W_max) * G;
-    const int pairs = d->B * d->Hkv;
-    static const int cand[][2] = {{4, 1}, {2, 2}, {1, 4}};
+    const int64_t pairs = static_cast<int64_t>(d->B) * d->Hkv;
+    static const int cand[][2] = {{8, 1}, {4, 1}, {4, 2}, {2, 4}, {1, 4}};
     Plan best{1, 4, 0, 0};
     const char *env = std::getenv("GR_ATTN_TILE");     // "NQT,NKS", tuning only
     int fq = 0, fk = 0;
@@ -139,17 +140,18 @@ Plan plan(const gr_decode_attn_dims *d)
         best.nks = fk;
     } else {
         for (const auto &c : cand) {
-            const int64_t n_qt = (M + 64 * c[0] - 1) / (64 * c[0]);
-            if (pairs * n_qt >= kCUs || (c[0] == 1)) {
-                best.nqt = c[0];
-                best.nks = c[1];
+            if (gr::fused_lds_bytes(d->D, c[0], c[1]) <= 0)
+                continue;
+            const int64_t n_qt = (M + 32 * c[0] - 1) / (32 * c[0]);
+            best.nqt = c[0];
+            best.nks = c[1];
+            if (pairs * n_qt * c[0] * c[1] >= 2 * kSIMDs)
                 break;
-            }
         }
     }
-    best.n_qt = static_cast<int>((M + 64 * best.nqt - 1) / (64 * best.nqt));
-    const int pairs_per_xcd = (pairs + 7) / 8;
-    best.grid = 8 * pairs_per_xcd * best.n_qt;
+    best.n_qt = static_cast<int>((M + 32 * best.nqt - 1) / (32 * best.nqt));
+    const int64_t pairs_per_xcd = (pairs + 7) / 8;
+    best.grid = static_cast<int>(8 * pairs_per_xcd * best.n_qt);
     return best;
 }
 

@@ -28,10 +28,11 @@ struct MetaCheck {
 constexpr int GENERIC_MAX_KEYS = 16320;
 
 // Fused-kernel instantiations: (head dim, query waves per stream NQT, key
-// streams NKS).  A workgroup has NQT*NKS waves and covers 64*NQT query rows.
-#define GR_FOR_EACH_FUSED_CONFIG(X) \
-    X(128, 1, 4) X(128, 2, 2) X(128, 4, 2) X(128, 4, 1) X(128, 2, 1) X(128, 1, 2) \
-    X(64, 1, 4) X(64, 2, 2) X(64, 4, 2) X(64, 4, 1) X(64, 2, 1) X(64, 1, 2)
+// streams NKS, LDS tile buffers per stream NBUF, target waves per SIMD OCC).
+// A workgroup has NQT*NKS waves and covers 32*NQT stacked query rows.
+#define GR_FOR_EACH_FUSED_CONFIG(X)                                            \
+    X(128, 2, 4, 2, 2) X(128, 4, 2, 2, 2) X(128, 4, 1, 3, 2) X(128, 8, 1, 3, 2)    \
+    X(128, 1, 4, 2, 2) X(64, 2, 4, 2, 2) X(64, 4, 2, 2, 2) X(64, 4, 1, 3, 2)
 
 int fused_lds_bytes(int D, int nqt, int nks);
 hipError_t launch_fused(const Params &p, int nqt, int nks, int grid, hipStream_t s);

@@ -9,29 +9,34 @@
 //
 // gfx950 mapping of the fused kernel (one launch does all three stages):
 //   * A workgroup owns one (request b, KV head g) pair and a tile of
-//     64*NQT stacked query rows: stacked row m = beam * G + i is query head
+//     32*NQT stacked query rows: stacked row m = beam * G + i is query head
 //     g*G+i of beam `beam`.  Its NQT*NKS waves form NKS key streams of NQT
 //     waves; stream ks walks a contiguous 1/NKS share of the context in
-//     32-key tiles staged through LDS (double buffered, one barrier per tile).
-//   * Each wave holds 64 query columns.  Scores are produced transposed,
+//     32-key tiles.  Tiles move HBM -> LDS with direct loads (no register
+//     staging), NBUF-deep, with one workgroup barrier per tile.
+//   * Each wave holds 32 query columns.  Scores are produced transposed,
 //     S^T = K * Q^T, with v_mfma_f32_32x32x16_bf16: the A operand is a K tile
 //     fragment read from LDS, the B operand is the wave's Q^T kept in
 //     registers for the whole pass.  In the 32x32 accumulator layout every
-//     lane holds 16 keys of ONE query, so the row max is an in-lane max3
+//     lane holds 16 keys of ONE query, so a row maximum is an in-lane max
 //     chain plus one v_permlane32_swap.
 //   * Probabilities are rounded to bf16 in registers and fed straight back
-//     as the B operand of O^T += V^T * P^T; the keys' order inside the
-//     contraction follows the accumulator layout, and V is stored transposed
-//     in LDS in that same order, so P never leaves registers.
+//     as the B operand of O^T += V^T * P^T.  The keys' order inside that
+//     contraction is the order in which the accumulator layout holds them;
+//     the matching V^T operand comes from transposing LDS reads
+//     (ds_read_b64_tr_b16) of the row-major V tile, so P never leaves
+//     registers and V is never transposed in memory.
 //   * Softmax in the log2 domain against a per-query reference maximum that
 //     stays fixed during the context sweep (the first tile's maximum), so the
 //     O^T accumulators are written only by the matrix cores inside the loop;
 //     a second, exact sweep runs only if a row sum leaves the safe range.
 //   * BeamKV steps are spread over the key streams; each stream folds its
-//     steps into its own running (max, sum, O) with vector loads along the
-//     BeamPath, before the streams merge through LDS by log-sum-exp.
+//     steps into its own (max, sum, O) with vector loads along the BeamPath,
+//     before the streams merge through LDS by log-sum-exp.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "gr_attn_internal.h"
 
@@ -43,6 +48,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int KT = 32;          // keys per context tile
 constexpr float SAFE_SUM = 1.8446744e19f;  // 2^64: largest row sum accepted in pass 0
@@ -51,24 +57,55 @@ constexpr uint32_t BF16_ONES = 0x3f803f80u;  // two bf16 ones
 
 template <int D>
 struct Geo {
-    static constexpr int KPITCH = D * 2 + 16;            // bytes per K row in LDS
-    static constexpr int VPITCH = KT * 2 + 16;           // bytes per transposed V row (one d)
-    static constexpr int KBYTES = KT * KPITCH;
-    static constexpr int VBYTES = D * VPITCH;
-    static constexpr int TILE = KBYTES + VBYTES;
-    static constexpr int STREAM = 2 * TILE;              // double buffered
+    static constexpr int ROW = D * 2;                    // bytes per K or V row in LDS
+    static constexpr int CH = D / 8;                     // 16-byte chunks per row
+    static constexpr int KBYTES = KT * ROW;
+    static constexpr int TILE = 2 * KBYTES;              // K tile then V tile
+    static constexpr int LOADS = TILE / 1024;            // 1 KB direct loads per tile
     static constexpr int DC = D / 16;                    // 16-wide d chunks (QK contraction)
     static constexpr int DB = D / 32;                    // 32-row d blocks of O^T
     static constexpr int OPITCH = (D + 4) * 4;           // bytes per query row in the merge area
-    static constexpr int OSLOT = 64 * OPITCH;            // one wave's O partial
+    static constexpr int OSLOT = 32 * OPITCH + 32 * 16;  // one wave's O partial + (max, sums)
 };
 
-template <int D, int NQT, int NKS>
+// XOR swizzles of the 16-byte chunks of a row (row-major K and V tiles, no
+// padding): the slot of chunk c of row r is c ^ f(r).  For K the 16 rows a
+// ds_read_b128 touches land in 16 different slots; for V the 4 rows x 4
+// chunks each half-wave touches in a transposing read are 16 different slots.
+template <int D>
+__device__ __forceinline__ int kswz(int r) { return r & (D / 8 - 1); }
+template <int D>
+__device__ __forceinline__ int vswz(int r) { return (4 * (r & 3)) & (D / 8 - 1); }
+
+template <int D, int NQT, int NKS, int NBUF>
 constexpr int lds_bytes()
 {
-    constexpr int stage = NKS * Geo<D>::STREAM;
-    constexpr int merge = (NKS - 1) * NQT * (Geo<D>::OSLOT + 64 * 8);
+    constexpr int stage = NKS * NBUF * Geo<D>::TILE;
+    constexpr int merge = (NKS - 1) * NQT * Geo<D>::OSLOT;
     return stage > merge ? stage : merge;
+}
+
+// One 1 KB direct global->LDS load: lane i of the wave writes bytes
+// [lds + 16 i, lds + 16 i + 16) from `g`.  Issued through inline assembly so
+// that the compiler does not serialise later LDS reads behind it; the kernel
+// waits for completion itself (vmcnt, then a workgroup barrier).
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+                 : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void block_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t *p)
@@ -98,14 +135,6 @@ __device__ __forceinline__ float swap32(float x, int h)
     return __uint_as_float(h ? lo : hi);
 }
 
-// position of key x (0..31) of a tile inside the transposed-V row: within
-// each 16-key chunk bits 2 and 3 are swapped, matching the order in which a
-// lane's accumulator registers hold the keys (see file comment)
-__device__ __forceinline__ int vpos(int x)
-{
-    return (x & 0x13) | ((x & 4) << 1) | ((x & 8) >> 1);
-}
-
 __device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float acc)
 {
     // vector elements are copied to scalars before the bit casts: a bit cast
@@ -127,11 +156,22 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
     return __builtin_bit_cast(uint32_t, v);
 }
 
-template <int D, int NQT, int NKS>
-__global__ __launch_bounds__(64 * NQT * NKS, 1) void fused_decode_attn(const Params p)
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Transposing LDS read: within each 16-lane group, lane i receives element
+// i%4 of the 8-byte words addressed by lanes i/4, 4+i/4, 8+i/4, 12+i/4.
+__device__ __forceinline__ i16x4 lds_tr16(const char *p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+}
+
+template <int D, int NQT, int NKS, int NBUF, int OCC>
+__global__ __launch_bounds__(64 * NQT * NKS) __attribute__((amdgpu_waves_per_eu(OCC)))
+void fused_decode_attn(const Params p)
 {
     using Gm = Geo<D>;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     // ---- work item: (pair, query tile), XCD-aware ----------------------
     // Workgroups are dispatched round-robin over the 8 XCDs; all query tiles
@@ -150,7 +190,7 @@ __global__ __launch_bounds__(64 * NQT * NKS, 1) void fused_decode_attn(const Par
     const int r0 = p.row_offset[b];
     const int Wb = p.row_offset[b + 1] - r0;
     const int M = Wb * G;
-    const int tile_row0 = qtile * 64 * NQT;
+    const int tile_row0 = qtile * 32 * NQT;
     if (tile_row0 >= M)
         return;                                   // uniform for the workgroup
     const int L = p.ctx_len[b];
@@ -163,208 +203,212 @@ __global__ __launch_bounds__(64 * NQT * NKS, 1) void fused_decode_attn(const Par
     const int ks = wave / NQT;
     const int h = lane >> 5;
     const int c32 = lane & 31;
-    const int wrow0 = tile_row0 + qt * 64;        // first stacked row of this wave
+    const int wrow0 = tile_row0 + qt * 32;        // first stacked row of this wave
     const bool wave_live = wrow0 < M;
 
-    // ---- Q^T fragments (B operand), resident for the whole pass -----------
-    u32x4 qf[2][Gm::DC];
-    int qrow[2];
-    bool qvalid[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int m = wrow0 + qb * 32 + c32;
-        qvalid[qb] = m < M;
-        const int w = qvalid[qb] ? m / G : 0;
-        const int i = qvalid[qb] ? m - w * G : 0;
-        qrow[qb] = r0 + w;
-        const uint16_t *src = p.q + ((int64_t)(r0 + w) * p.Hq + g * G + i) * D + 8 * h;
+    // ---- the lane's query column and its Q^T fragments (B operand) -------
+    const int m_row = wrow0 + c32;
+    const bool qvalid = m_row < M;
+    const int beam = qvalid ? m_row / G : 0;
+    const int qhead = g * G + (qvalid ? m_row - beam * G : 0);
+    const int qrow = r0 + beam;
+    u32x4 qf[Gm::DC];
+    {
+        const uint16_t *src = p.q + ((int64_t)qrow * p.Hq + qhead) * D + 8 * h;
 #pragma unroll
         for (int c = 0; c < Gm::DC; ++c)
-            qf[qb][c] = qvalid[qb] ? ldg16(src + 16 * c) : u32x4{0, 0, 0, 0};
+            qf[c] = qvalid ? ldg16(src + 16 * c) : u32x4{0, 0, 0, 0};
+        // consume the loads here, so that no wait for them is left inside
+        // the tile loop (where it would also wait for the tile prefetches)
+#pragma unroll
+        for (int c = 0; c < Gm::DC; ++c)
+            asm volatile("" : "+v"(qf[c]));
     }
 
-    float m_ref[2] = {NEG_INF, NEG_INF};          // reference maximum, log2 units
-    float l_run[2] = {0.f, 0.f};                  // this lane-half's share of the sum
-    f32x16 acc[2][Gm::DB];
+    float m_ref = NEG_INF;                        // reference maximum, log2 units
+    // this lane-half's share of the row sum, twice: l_run adds the bf16
+    // values the matrix cores multiply (it normalises the output, so the
+    // weights sum to one exactly); l_lse adds the unrounded values (it
+    // gives the log-sum-exp, free of the bf16 rounding of the weights)
+    float l_run = 0.f;
+    float l_lse = 0.f;
+    f32x16 acc[Gm::DB];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int db = 0; db < Gm::DB; ++db)
-            acc[qb][db] = f32x16{};
+    for (int db = 0; db < Gm::DB; ++db)
+        acc[db] = f32x16{};
     const float cs = p.scale_log2;
 
     // ---- shared (context) stage -----------------------------------------
     const int n_tiles = (L + KT - 1) / KT;
     const int t_begin = (ks * n_tiles) / NKS;
-    const int t_end = ((ks + 1) * n_tiles) / NKS;
+    const int n_mine = ((ks + 1) * n_tiles) / NKS - t_begin;
     const int iters = (n_tiles + NKS - 1) / NKS;  // same for every wave (barrier count)
-    char *stream_lds = smem + ks * Gm::STREAM;
-    const int64_t kv_base = ((int64_t)b * p.ctx_cap * p.Hkv + g) * D;
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
+    const uint32_t stream_lds = lds0 + ks * (NBUF * Gm::TILE);
+    const char *stream_ptr = smem + ks * (NBUF * Gm::TILE);
+    const uint16_t *kv_k = p.ctx_k + ((int64_t)b * p.ctx_cap * p.Hkv + g) * D;
+    const uint16_t *kv_v = p.ctx_v + ((int64_t)b * p.ctx_cap * p.Hkv + g) * D;
     const int64_t kv_tok = (int64_t)p.Hkv * D;    // elements between consecutive tokens
-    const int lt = qt * 64 + lane;                // loader id inside the stream
+    constexpr int RPL = 1024 / Gm::ROW;           // rows covered by one 1 KB load
+    constexpr int LPW = (Gm::LOADS + NQT - 1) / NQT;   // loads per wave per tile (max)
 
-    constexpr int K_CHUNKS = KT * D / 8;          // 16-byte pieces of a K tile
-    constexpr int K_PER = (K_CHUNKS + 64 * NQT - 1) / (64 * NQT);
-    constexpr int V_UNITS = (KT / 2) * (D / 8);   // (key pair, d octet) units of a V tile
-    constexpr int V_PER = (V_UNITS + 64 * NQT - 1) / (64 * NQT);
-    u32x4 kreg[K_PER];
-    u32x4 vreg[V_PER][2];
-
-    auto load_tile = [&](int t) {
-        const int kbase = t * KT;
+    // Issue this wave's share of the direct loads of stream tile `t` into
+    // buffer `buf`.  Load u < LOADS/2 fills K rows, the rest V rows; rows
+    // past the context end repeat row L-1 (their scores are masked and their
+    // probabilities are 0, so the repeated values never contribute).
+    auto issue_tile = [&](int t, int buf) {
+        const int key0 = (t_begin + t) * KT;
+        const uint32_t dst = stream_lds + buf * Gm::TILE;
 #pragma unroll
-        for (int i = 0; i < K_PER; ++i) {
-            const int u = lt + i * 64 * NQT;
-            const int row = u / (D / 8), col = u % (D / 8);
-            const int key = kbase + row;
-            kreg[i] = (u < K_CHUNKS && key < L)
-                          ? ldg16(p.ctx_k + kv_base + key * kv_tok + col * 8)
-                          : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int i = 0; i < V_PER; ++i) {
-            const int u = lt + i * 64 * NQT;
-            const int kp = u / (D / 8), oc = u % (D / 8);
-            const int key = kbase + 2 * kp;
-            const bool ok = u < V_UNITS;
-            vreg[i][0] = (ok && key < L) ? ldg16(p.ctx_v + kv_base + key * kv_tok + oc * 8)
-                                         : u32x4{0, 0, 0, 0};
-            vreg[i][1] = (ok && key + 1 < L)
-                             ? ldg16(p.ctx_v + kv_base + (key + 1) * kv_tok + oc * 8)
-                             : u32x4{0, 0, 0, 0};
-        }
-    };
-    auto store_tile = [&](int buf) {
-        char *kl = stream_lds + buf * Gm::TILE;
-        char *vl = kl + Gm::KBYTES;
-#pragma unroll
-        for (int i = 0; i < K_PER; ++i) {
-            const int u = lt + i * 64 * NQT;
-            if (u < K_CHUNKS) {
-                const int row = u / (D / 8), col = u % (D / 8);
-                *reinterpret_cast<u32x4 *>(kl + row * Gm::KPITCH + col * 16) = kreg[i];
+        for (int i = 0; i < LPW; ++i) {
+            const int u = qt + i * NQT;
+            if (u < Gm::LOADS) {
+                const bool is_v = u >= Gm::LOADS / 2;
+                const int uu = is_v ? u - Gm::LOADS / 2 : u;
+                const int r = uu * RPL + lane / Gm::CH;    // tile row written by this lane
+                const int s = lane % Gm::CH;               // its 16-byte slot in that row
+                const int c = s ^ (is_v ? vswz<D>(r) : kswz<D>(r));
+                int key = key0 + r;
+                key = key < L ? key : L - 1;
+                const uint16_t *src = (is_v ? kv_v : kv_k) + key * kv_tok + 8 * c;
+                dma16(src, __builtin_amdgcn_readfirstlane(dst + (is_v ? Gm::KBYTES : 0) +
+                                                          uu * 1024));
             }
         }
+    };
+    // loads this wave issues per tile (waves of a stream share LOADS)
+    const int my_loads = (Gm::LOADS - qt + NQT - 1) / NQT;
+    // wait until at most `pending` later tiles of this wave are still loading
+    auto wait_tiles = [&](int pending) {
+        const int n = pending > 0 ? pending * my_loads : 0;
+        if (n >= 48)
+            wait_vm<48>();
+        else if (n >= 32)
+            wait_vm<32>();
+        else if (n >= 16)
+            wait_vm<16>();
+        else if (n >= 8)
+            wait_vm<8>();
+        else if (n >= 4)
+            wait_vm<4>();
+        else if (n >= 2)
+            wait_vm<2>();
+        else
+            wait_vm<0>();
+    };
+
+    // Per-tile compute of a live wave.  ACCUM: p = exp2(s*c - m_ref) against
+    // the fixed reference; otherwise only the exact maxima are tracked.  The
+    // accumulators are written only by the matrix cores, on every iteration
+    // of the compute loop, so they stay in accumulation registers.
+    auto compute_tile = [&](int it, bool want_max, auto accum_tag) {
+        constexpr bool ACCUM = decltype(accum_tag)::value;
+        const char *kl = stream_ptr + (it % NBUF) * Gm::TILE;
+        const char *vl = kl + Gm::KBYTES;
+        const int kbase = (t_begin + it) * KT;
+        // S^T = K * Q^T: K fragment of lane row c32, d chunk 2c+h
+        f32x16 s = f32x16{};
 #pragma unroll
-        for (int i = 0; i < V_PER; ++i) {
-            const int u = lt + i * 64 * NQT;
-            if (u < V_UNITS) {
-                const int kp = u / (D / 8), oc = u % (D / 8);
-                char *dst = vl + (8 * oc) * Gm::VPITCH + vpos(2 * kp) * 2;
+        for (int c = 0; c < Gm::DC; ++c) {
+            const u32x4 kf = *reinterpret_cast<const u32x4 *>(
+                kl + c32 * Gm::ROW + 16 * ((2 * c + h) ^ kswz<D>(c32)));
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf),
+                                                        __builtin_bit_cast(bf16x8, qf[c]), s, 0,
+                                                        0, 0);
+        }
+        if (kbase + KT > L) {                      // keys past the context end
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kbase + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (key >= L)
+                    s[r] = NEG_INF;
+            }
+        }
+        if (want_max) {
+            float mx = s[0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r)
+                mx = __builtin_fmaxf(mx, s[r]);
+            mx = __builtin_fmaxf(mx, swap32(mx, h));
+            m_ref = __builtin_fmaxf(m_ref, mx * cs);
+        }
+        if constexpr (ACCUM) {
+            // probabilities as bf16 B operands; the row sum adds the rounded
+            // values, so the normalisation matches the weighted sum the
+            // matrix cores form
+            u32x4 pb[2];
+            const float nm = -m_ref;
+            float sum = l_run, sum_x = l_lse;
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const uint32_t a = vreg[i][0][e], c = vreg[i][1][e];
-                    *reinterpret_cast<uint32_t *>(dst + (2 * e) * Gm::VPITCH) =
-                        __builtin_amdgcn_perm(c, a, 0x05040100u);
-                    *reinterpret_cast<uint32_t *>(dst + (2 * e + 1) * Gm::VPITCH) =
-                        __builtin_amdgcn_perm(c, a, 0x07060302u);
+                    const int r = 8 * kc + 2 * e;
+                    const float p0 = exp2_fast(__builtin_fmaf(s[r], cs, nm));
+                    const float p1 = exp2_fast(__builtin_fmaf(s[r + 1], cs, nm));
+                    const uint32_t pk = pack_bf16(p0, p1);
+                    pb[kc][e] = pk;
+                    sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
+                                                          __builtin_bit_cast(bf16x2, BF16_ONES),
+                                                          sum, false);
+                    sum_x += p0 + p1;
                 }
-            }
+            l_run = sum;
+            l_lse = sum_x;
+            // O^T += V^T * P^T.  V^T fragments come from transposing reads
+            // of the row-major V tile: lane group (h, dh) reads keys
+            // 16kc+4h+{0..3} (then +8) at d = 32db+16dh+{0..15}
+            const int dh = (lane >> 4) & 1;
+            const int sl = lane & 15;
+#pragma unroll
+            for (int db = 0; db < Gm::DB; ++db)
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) {
+                    const int key_a = 16 * kc + 4 * h + (sl >> 2);
+                    const int key_b = key_a + 8;
+                    const int cidx = 4 * db + 2 * dh + ((sl & 3) >> 1);
+                    const int boff = 8 * (sl & 1);
+                    const i16x4 va =
+                        lds_tr16(vl + key_a * Gm::ROW + 16 * (cidx ^ vswz<D>(key_a)) + boff);
+                    const i16x4 vb =
+                        lds_tr16(vl + key_b * Gm::ROW + 16 * (cidx ^ vswz<D>(key_b)) + boff);
+                    const bf16x8 vf = __builtin_shufflevector(
+                        __builtin_bit_cast(bf16x4_t, va), __builtin_bit_cast(bf16x4_t, vb), 0, 1,
+                        2, 3, 4, 5, 6, 7);
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        vf, __builtin_bit_cast(bf16x8, pb[kc]), acc[db], 0, 0, 0);
+                }
         }
     };
 
-    // One sweep over the stream's tiles.  ACCUM: p = exp2(s*c - m_ref) with a
-    // fixed per-query reference m_ref (taken from the stream's first tile
-    // unless `given_ref`); the accumulators are touched only by the matrix
-    // cores inside the loop.  MAXONLY: exact per-query maxima, no values.
-    auto sweep = [&](bool accum, bool given_ref) {
-        if (iters > 0) {
-            if (t_begin < t_end) {
-                load_tile(t_begin);
-                store_tile(0);
+    // One sweep over the stream's tiles with NBUF-deep direct-load
+    // prefetch and one workgroup barrier per tile.  Every wave executes the
+    // same number of barriers; waves without query rows only load.
+    auto sweep = [&](bool first_max, auto accum_tag) {
+#pragma unroll
+        for (int t = 0; t < NBUF - 1; ++t)
+            if (t < n_mine)
+                issue_tile(t, t);
+        auto step = [&](int it) {
+            const int issued_last = (it + NBUF - 2 < n_mine - 1) ? it + NBUF - 2 : n_mine - 1;
+            wait_tiles(issued_last - it);
+            block_barrier();
+            if (it + NBUF - 1 < n_mine)
+                issue_tile(it + NBUF - 1, (it + NBUF - 1) % NBUF);
+        };
+        if (wave_live) {
+            for (int it = 0; it < n_mine; ++it) {
+                step(it);
+                compute_tile(it, first_max && it == 0, accum_tag);
             }
-            __syncthreads();
+            for (int it = n_mine; it < iters; ++it)
+                step(it);
+        } else {
+            for (int it = 0; it < iters; ++it)
+                step(it);
         }
-        for (int it = 0; it < iters; ++it) {
-            const int t = t_begin + it;
-            const bool active = t < t_end;
-            const bool has_next = t + 1 < t_end;
-            if (has_next)
-                load_tile(t + 1);
-            if (active && wave_live) {
-                const char *kl = stream_lds + (it & 1) * Gm::TILE;
-                const char *vl = kl + Gm::KBYTES;
-                // S^T = K * Q^T for both query blocks
-                f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-                for (int c = 0; c < Gm::DC; ++c) {
-                    const u32x4 a = *reinterpret_cast<const u32x4 *>(kl + c32 * Gm::KPITCH +
-                                                                     (2 * c + h) * 16);
-                    const bf16x8 av = __builtin_bit_cast(bf16x8, a);
-                    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        av, __builtin_bit_cast(bf16x8, qf[0][c]), s[0], 0, 0, 0);
-                    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        av, __builtin_bit_cast(bf16x8, qf[1][c]), s[1], 0, 0, 0);
-                }
-                // keys past the context end (only in the last tile)
-                const int kbase = t * KT;
-                if (kbase + KT > L) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = kbase + 8 * (r >> 2) + 4 * h + (r & 3);
-                        if (key >= L) {
-                            s[0][r] = NEG_INF;
-                            s[1][r] = NEG_INF;
-                        }
-                    }
-                }
-                if (!accum || (it == 0 && !given_ref)) {
-#pragma unroll
-                    for (int qb = 0; qb < 2; ++qb) {
-                        float mx = s[qb][0];
-#pragma unroll
-                        for (int r = 1; r < 16; ++r)
-                            mx = __builtin_fmaxf(mx, s[qb][r]);
-                        mx = __builtin_fmaxf(mx, swap32(mx, h));
-                        m_ref[qb] = __builtin_fmaxf(m_ref[qb], mx * cs);
-                    }
-                }
-                if (accum) {
-                    // probabilities, row sums, bf16 B operands
-                    u32x4 pb[2][2];
-#pragma unroll
-                    for (int qb = 0; qb < 2; ++qb) {
-                        const float nm = -m_ref[qb];
-                        float pr[16];
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            pr[r] = exp2_fast(__builtin_fmaf(s[qb][r], cs, nm));
-                        // the row sum adds the bf16-rounded probabilities that
-                        // the matrix cores multiply, so the normalisation
-                        // matches the weighted sum exactly
-                        float sum = l_run[qb];
-#pragma unroll
-                        for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const uint32_t pk =
-                                    pack_bf16(pr[8 * kc + 2 * e], pr[8 * kc + 2 * e + 1]);
-                                pb[qb][kc][e] = pk;
-                                sum = __builtin_amdgcn_fdot2_f32_bf16(
-                                    __builtin_bit_cast(bf16x2, pk),
-                                    __builtin_bit_cast(bf16x2, BF16_ONES), sum, false);
-                            }
-                        l_run[qb] = sum;
-                    }
-                    // O^T += V^T * P^T
-#pragma unroll
-                    for (int db = 0; db < Gm::DB; ++db)
-#pragma unroll
-                        for (int kc = 0; kc < 2; ++kc) {
-                            const u32x4 a = *reinterpret_cast<const u32x4 *>(
-                                vl + (32 * db + c32) * Gm::VPITCH + (16 * kc + 8 * h) * 2);
-                            const bf16x8 av = __builtin_bit_cast(bf16x8, a);
-                            acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                av, __builtin_bit_cast(bf16x8, pb[0][kc]), acc[0][db], 0, 0, 0);
-                            acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                av, __builtin_bit_cast(bf16x8, pb[1][kc]), acc[1][db], 0, 0, 0);
-                        }
-                }
-            }
-            if (has_next)
-                store_tile((it + 1) & 1);
-            __syncthreads();
-        }
+        wait_vm<0>();
+        block_barrier();                           // buffers free for the next user
     };
 
     // Pass 0 takes each stream's first-tile maximum as the fixed reference:
@@ -373,147 +417,129 @@ __global__ __launch_bounds__(64 * NQT * NKS, 1) void fused_decode_attn(const Par
     // normalisation is exact.  Otherwise (scores rising by more than ~44
     // nats along the context) the workgroup sweeps again: exact maxima
     // first, then the accumulation against them.
-    sweep(true, false);
-    {
-        bool bad = false;
+    sweep(true, std::true_type{});
+    if (__syncthreads_or(qvalid && !(l_lse < SAFE_SUM))) {
+        m_ref = NEG_INF;
+        l_run = 0.f;
+        l_lse = 0.f;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-            bad |= qvalid[qb] && !(l_run[qb] < SAFE_SUM);
-        if (__syncthreads_or(bad)) {
-            m_ref[0] = m_ref[1] = NEG_INF;
-            l_run[0] = l_run[1] = 0.f;
+        for (int db = 0; db < Gm::DB; ++db)
+            acc[db] = f32x16{};
+        sweep(true, std::false_type{});
+        sweep(false, std::true_type{});
+    }
+
+    // The vector-unit stages below work on a copy of the accumulators pinned
+    // in ordinary VGPRs; the context loop above then keeps its accumulators
+    // in the matrix cores' accumulation registers without per-iteration moves.
+    f32x16 o[Gm::DB];
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int db = 0; db < Gm::DB; ++db)
-                    acc[qb][db] = f32x16{};
-            sweep(false, false);
-            sweep(true, true);
-        }
+    for (int db = 0; db < Gm::DB; ++db) {
+        o[db] = acc[db];
+        asm volatile("" : "+v"(o[db]));
     }
 
     // ---- per-beam stage: BeamKV steps ks, ks+NKS, ... along BeamPath ------
     if (wave_live) {
         for (int s = ks; s < T; s += NKS) {
+            const int idx = qvalid ? p.beam_path[(int64_t)qrow * p.T_cap + s] : 0;
+            const int64_t base = (((int64_t)b * p.beam_cap + idx) * p.Hkv + g) * D;
+            const uint16_t *kr = p.beam_k + base + 8 * h;
+            float dot = 0.f;
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const int idx = qvalid[qb] ? p.beam_path[(int64_t)qrow[qb] * p.T_cap + s] : 0;
-                const int64_t base = (((int64_t)b * p.beam_cap + idx) * p.Hkv + g) * D;
-                const uint16_t *kr = p.beam_k + base + 8 * h;
-                float dot = 0.f;
+            for (int c = 0; c < Gm::DC; ++c)
+                dot = dot8(qf[c], qvalid ? ldg16(kr + 16 * c) : u32x4{0, 0, 0, 0}, dot);
+            dot += swap32(dot, h);
+            const float tz = dot * cs;
+            const float mn = __builtin_fmaxf(m_ref, tz);
+            const float alpha = exp2_fast(m_ref - mn);
+            const float pw = exp2_fast(tz - mn);
+            m_ref = mn;
+            l_run = l_run * alpha + (h == 0 ? pw : 0.f);
+            l_lse = l_lse * alpha + (h == 0 ? pw : 0.f);
+            const uint16_t *vr = p.beam_v + base + 4 * h;
 #pragma unroll
-                for (int c = 0; c < Gm::DC; ++c)
-                    dot = dot8(qf[qb][c], qvalid[qb] ? ldg16(kr + 16 * c) : u32x4{0, 0, 0, 0},
-                               dot);
-                dot += swap32(dot, h);
-                const float tz = dot * cs;
-                const float mn = __builtin_fmaxf(m_ref[qb], tz);
-                const float alpha = exp2_fast(m_ref[qb] - mn);
-                const float pw = exp2_fast(tz - mn);
-                m_ref[qb] = mn;
-                l_run[qb] = l_run[qb] * alpha + (h == 0 ? pw : 0.f);
-                const uint16_t *vr = p.beam_v + base + 4 * h;
+            for (int db = 0; db < Gm::DB; ++db)
 #pragma unroll
-                for (int db = 0; db < Gm::DB; ++db)
-#pragma unroll
-                    for (int rg = 0; rg < 4; ++rg) {
-                        const u32x2 v = qvalid[qb] ? ldg8(vr + 32 * db + 8 * rg) : u32x2{0, 0};
-                        f32x16 &o = acc[qb][db];
-                        o[4 * rg + 0] = o[4 * rg + 0] * alpha + pw * bf16lo(v[0]);
-                        o[4 * rg + 1] = o[4 * rg + 1] * alpha + pw * bf16hi(v[0]);
-                        o[4 * rg + 2] = o[4 * rg + 2] * alpha + pw * bf16lo(v[1]);
-                        o[4 * rg + 3] = o[4 * rg + 3] * alpha + pw * bf16hi(v[1]);
-                    }
-            }
+                for (int rg = 0; rg < 4; ++rg) {
+                    const u32x2 v = qvalid ? ldg8(vr + 32 * db + 8 * rg) : u32x2{0, 0};
+                    f32x16 &ov = o[db];
+                    ov[4 * rg + 0] = ov[4 * rg + 0] * alpha + pw * bf16lo(v[0]);
+                    ov[4 * rg + 1] = ov[4 * rg + 1] * alpha + pw * bf16hi(v[0]);
+                    ov[4 * rg + 2] = ov[4 * rg + 2] * alpha + pw * bf16lo(v[1]);
+                    ov[4 * rg + 3] = ov[4 * rg + 3] * alpha + pw * bf16hi(v[1]);
+                }
         }
     }
     // full row sums (the two lane halves held different keys)
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-        l_run[qb] += swap32(l_run[qb], h);
+    l_run += swap32(l_run, h);
+    l_lse += swap32(l_lse, h);
 
     // ---- merge of the key streams through LDS (log-sum-exp) ---------------
     if constexpr (NKS > 1) {
         char *ml = smem;                           // staging buffers are free now
         if (ks > 0 && wave_live) {
-            const int slot = (ks - 1) * NQT + qt;
-            char *o = ml + slot * (Gm::OSLOT + 64 * 8);
-            float *stats = reinterpret_cast<float *>(o + Gm::OSLOT);
+            char *sp = ml + ((ks - 1) * NQT + qt) * Gm::OSLOT;
+            float *stats = reinterpret_cast<float *>(sp + 32 * Gm::OPITCH);
+            if (h == 0) {
+                stats[4 * c32] = m_ref;
+                stats[4 * c32 + 1] = l_run;
+                stats[4 * c32 + 2] = l_lse;
+            }
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const int qc = qb * 32 + c32;
-                if (h == 0) {
-                    stats[2 * qc] = m_ref[qb];
-                    stats[2 * qc + 1] = l_run[qb];
+            for (int db = 0; db < Gm::DB; ++db)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const f32x4 v = {o[db][4 * rg], o[db][4 * rg + 1], o[db][4 * rg + 2],
+                                     o[db][4 * rg + 3]};
+                    *reinterpret_cast<f32x4 *>(sp + c32 * Gm::OPITCH +
+                                               (32 * db + 8 * rg + 4 * h) * 4) = v;
                 }
+        }
+        __syncthreads();
+        if (ks == 0 && wave_live) {
+#pragma unroll
+            for (int k2 = 1; k2 < NKS; ++k2) {
+                const char *sp = ml + ((k2 - 1) * NQT + qt) * Gm::OSLOT;
+                const float *stats = reinterpret_cast<const float *>(sp + 32 * Gm::OPITCH);
+                const float mo = stats[4 * c32], lo = stats[4 * c32 + 1];
+                const float lxo = stats[4 * c32 + 2];
+                const float mn = __builtin_fmaxf(m_ref, mo);
+                const float a = m_ref == NEG_INF ? 0.f : exp2_fast(m_ref - mn);
+                const float bw = mo == NEG_INF ? 0.f : exp2_fast(mo - mn);
+                m_ref = mn;
+                l_run = l_run * a + lo * bw;
+                l_lse = l_lse * a + lxo * bw;
 #pragma unroll
                 for (int db = 0; db < Gm::DB; ++db)
 #pragma unroll
                     for (int rg = 0; rg < 4; ++rg) {
-                        f32x4 v = {acc[qb][db][4 * rg], acc[qb][db][4 * rg + 1],
-                                   acc[qb][db][4 * rg + 2], acc[qb][db][4 * rg + 3]};
-                        *reinterpret_cast<f32x4 *>(o + qc * Gm::OPITCH +
-                                                   (32 * db + 8 * rg + 4 * h) * 4) = v;
+                        const f32x4 v = *reinterpret_cast<const f32x4 *>(
+                            sp + c32 * Gm::OPITCH + (32 * db + 8 * rg + 4 * h) * 4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            o[db][4 * rg + e] = o[db][4 * rg + e] * a + v[e] * bw;
                     }
-            }
-        }
-        __syncthreads();
-        if (ks == 0 && wave_live) {
-            for (int k2 = 1; k2 < NKS; ++k2) {
-                const int slot = (k2 - 1) * NQT + qt;
-                const char *o = ml + slot * (Gm::OSLOT + 64 * 8);
-                const float *stats = reinterpret_cast<const float *>(o + Gm::OSLOT);
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    const int qc = qb * 32 + c32;
-                    const float mo = stats[2 * qc], lo = stats[2 * qc + 1];
-                    const float mn = __builtin_fmaxf(m_ref[qb], mo);
-                    const float a = m_ref[qb] == NEG_INF ? 0.f : exp2_fast(m_ref[qb] - mn);
-                    const float bw = mo == NEG_INF ? 0.f : exp2_fast(mo - mn);
-                    m_ref[qb] = mn;
-                    l_run[qb] = l_run[qb] * a + lo * bw;
-#pragma unroll
-                    for (int db = 0; db < Gm::DB; ++db)
-#pragma unroll
-                        for (int rg = 0; rg < 4; ++rg) {
-                            const f32x4 v = *reinterpret_cast<const f32x4 *>(
-                                o + qc * Gm::OPITCH + (32 * db + 8 * rg + 4 * h) * 4);
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                acc[qb][db][4 * rg + e] = acc[qb][db][4 * rg + e] * a + v[e] * bw;
-                        }
-                }
             }
         }
     }
 
     // ---- epilogue: normalise, bf16 output, fp32 natural-log LSE ----------
-    if (ks == 0 && wave_live) {
+    if (ks == 0 && wave_live && qvalid) {
+        const int64_t orow = (int64_t)qrow * p.Hq + qhead;
+        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+        uint16_t *dst = p.out + orow * D + 4 * h;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            if (!qvalid[qb])
-                continue;
-            const int m = wrow0 + qb * 32 + c32;
-            const int w = m / G;
-            const int i = m - w * G;
-            const int hq = g * G + i;
-            const int64_t orow = ((int64_t)(r0 + w) * p.Hq + hq);
-            const float l = l_run[qb];
-            const float inv = l > 0.f ? 1.f / l : 0.f;
-            uint16_t *dst = p.out + orow * D + 4 * h;
+        for (int db = 0; db < Gm::DB; ++db)
 #pragma unroll
-            for (int db = 0; db < Gm::DB; ++db)
-#pragma unroll
-                for (int rg = 0; rg < 4; ++rg) {
-                    const f32x16 &o = acc[qb][db];
-                    u32x2 v = {pack_bf16(o[4 * rg] * inv, o[4 * rg + 1] * inv),
-                               pack_bf16(o[4 * rg + 2] * inv, o[4 * rg + 3] * inv)};
-                    *reinterpret_cast<u32x2 *>(dst + 32 * db + 8 * rg) = v;
-                }
-            if (h == 0)
-                p.lse[orow] = l > 0.f ? (m_ref[qb] + __builtin_log2f(l)) * 0.69314718055994531f
+            for (int rg = 0; rg < 4; ++rg) {
+                const u32x2 v = {pack_bf16(o[db][4 * rg] * inv, o[db][4 * rg + 1] * inv),
+                                 pack_bf16(o[db][4 * rg + 2] * inv, o[db][4 * rg + 3] * inv)};
+                *reinterpret_cast<u32x2 *>(dst + 32 * db + 8 * rg) = v;
+            }
+        if (h == 0)
+            p.lse[orow] = l_lse > 0.f ? (m_ref + __builtin_log2f(l_lse)) * 0.69314718055994531f
                                       : NEG_INF;
-        }
     }
 }
 
@@ -631,11 +657,11 @@ __global__ void check_metadata(const MetaCheck c)
 __global__ void zero_i32(int32_t *p) { *p = 0; }
 
 // ---------------------------------------------------------------------------
-template <int D, int NQT, int NKS>
+template <int D, int NQT, int NKS, int NBUF, int OCC>
 static hipError_t launch_fused_t(const Params &p, int grid, hipStream_t s)
 {
-    constexpr int lds = lds_bytes<D, NQT, NKS>();
-    auto kern = fused_decode_attn<D, NQT, NKS>;
+    constexpr int lds = lds_bytes<D, NQT, NKS, NBUF>();
+    auto kern = fused_decode_attn<D, NQT, NKS, NBUF, OCC>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess)
@@ -646,9 +672,9 @@ static hipError_t launch_fused_t(const Params &p, int grid, hipStream_t s)
 
 int fused_lds_bytes(int D, int nqt, int nks)
 {
-#define GR_LDS_CASE(d, a, c)                                                          \
+#define GR_LDS_CASE(d, a, c, nb, oc)                                                  \
     if (D == d && nqt == a && nks == c)                                               \
-        return lds_bytes<d, a, c>();
+        return lds_bytes<d, a, c, nb>();
     GR_FOR_EACH_FUSED_CONFIG(GR_LDS_CASE)
 #undef GR_LDS_CASE
     return -1;
@@ -656,9 +682,9 @@ int fused_lds_bytes(int D, int nqt, int nks)
 
 hipError_t launch_fused(const Params &p, int nqt, int nks, int grid, hipStream_t s)
 {
-#define GR_LAUNCH_CASE(d, a, c)                                                       \
+#define GR_LAUNCH_CASE(d, a, c, nb, oc)                                               \
     if (p.D == d && nqt == a && nks == c)                                             \
-        return launch_fused_t<d, a, c>(p, grid, s);
+        return launch_fused_t<d, a, c, nb, oc>(p, grid, s);
     GR_FOR_EACH_FUSED_CONFIG(GR_LAUNCH_CASE)
 #undef GR_LAUNCH_CASE
     return hipErrorInvalidValue;
