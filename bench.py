@@ -158,8 +158,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--only-secondary", action="store_true",
-                    help="measure only the 900-beam workload (profiling runs)")
+    ap.add_argument("--only", choices=["primary", "secondary"],
+                    help="time one workload only and print its launch time (profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run 10 device copies of 256 MiB (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path "
@@ -172,10 +174,18 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
 
-    if args.only_secondary:
-        sec = measure(SECONDARY, args.steps, args.warmup)
-        print(json.dumps({"workload": sec["inp"].wl.name, "launch_us": sec["launch_ms"] * 1e3,
-                          "ms_per_step": sec["ms_per_step"]}), flush=True)
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": 256 << 20, "launches": 10}), flush=True)
+        return
+    if args.only:
+        r = measure(PRIMARY if args.only == "primary" else SECONDARY, args.steps, args.warmup)
+        print(json.dumps({"workload": r["inp"].wl.name, "launch_us": r["launch_ms"] * 1e3,
+                          "ms_per_step": r["ms_per_step"]}), flush=True)
         return
     prim = measure(PRIMARY, args.steps, args.warmup)
     inp = prim["inp"]

@@ -125,13 +125,14 @@ struct Plan {
 };
 
 constexpr int kSIMDs = 256 * 4;
+constexpr int kLdsBytes = 160 * 1024;     // LDS per compute unit
 
 Plan plan(const gr_decode_attn_dims *d)
 {
     const int G = d->Hq / d->Hkv;
     const int64_t M = static_cast<int64_t>(d->W_max) * G;
     const int64_t pairs = static_cast<int64_t>(d->B) * d->Hkv;
-    static const int cand[][2] = {{8, 1}, {4, 1}, {4, 2}, {2, 4}, {1, 4}};
+    static const int cand[][2] = {{8, 1}, {4, 1}, {4, 2}, {2, 2}, {2, 4}};
     Plan best{1, 4, 0, 0};
     const char *env = std::getenv("GR_ATTN_TILE");     // "NQT,NKS", tuning only
     int fq = 0, fk = 0;
@@ -140,7 +141,8 @@ Plan plan(const gr_decode_attn_dims *d)
         best.nks = fk;
     } else {
         for (const auto &c : cand) {
-            if (gr::fused_lds_bytes(d->D, c[0], c[1]) <= 0)
+            const int lds = gr::fused_lds_bytes(d->D, c[0], c[1]);
+            if (lds <= 0 || lds > kLdsBytes)
                 continue;
             const int64_t n_qt = (M + 32 * c[0] - 1) / (32 * c[0]);
             best.nqt = c[0];

@@ -31,8 +31,8 @@ constexpr int GENERIC_MAX_KEYS = 16320;
 // streams NKS, LDS tile buffers per stream NBUF, target waves per SIMD OCC).
 // A workgroup has NQT*NKS waves and covers 32*NQT stacked query rows.
 #define GR_FOR_EACH_FUSED_CONFIG(X)                                            \
-    X(128, 2, 4, 2, 2) X(128, 4, 2, 2, 2) X(128, 4, 1, 3, 2) X(128, 8, 1, 3, 2)    \
-    X(128, 1, 4, 2, 2) X(64, 2, 4, 2, 2) X(64, 4, 2, 2, 2) X(64, 4, 1, 3, 2)
+    X(128, 8, 1, 4, 2) X(128, 4, 1, 4, 2) X(128, 4, 2, 4, 2) X(128, 2, 2, 4, 2)    \
+    X(64, 4, 1, 4, 2) X(64, 2, 2, 4, 2) X(64, 2, 4, 3, 2)
 
 int fused_lds_bytes(int D, int nqt, int nks);
 hipError_t launch_fused(const Params &p, int nqt, int nks, int grid, hipStream_t s);

@@ -95,6 +95,19 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds)
                  : "memory", "m0");
 }
 
+// Same, with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte
+// offset (no 64-bit address arithmetic per lane).
+__device__ __forceinline__ void dma16_s(const void *base, uint32_t off, uint32_t lds)
+{
+    // base and lds are wave-uniform; make that explicit so they live in SGPRs
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sb),
+                 "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm()
 {
@@ -197,7 +210,7 @@ void fused_decode_attn(const Params p)
     const int T = p.beam_len[b];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int lane = tid & 63;
     const int qt = wave % NQT;
     const int ks = wave / NQT;
@@ -244,35 +257,48 @@ void fused_decode_attn(const Params p)
     const int n_mine = ((ks + 1) * n_tiles) / NKS - t_begin;
     const int iters = (n_tiles + NKS - 1) / NKS;  // same for every wave (barrier count)
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
-    const uint32_t stream_lds = lds0 + ks * (NBUF * Gm::TILE);
-    const char *stream_ptr = smem + ks * (NBUF * Gm::TILE);
+    const uint32_t stream_off = ks * (NBUF * Gm::TILE);        // byte offset of this stream
     const uint16_t *kv_k = p.ctx_k + ((int64_t)b * p.ctx_cap * p.Hkv + g) * D;
     const uint16_t *kv_v = p.ctx_v + ((int64_t)b * p.ctx_cap * p.Hkv + g) * D;
-    const int64_t kv_tok = (int64_t)p.Hkv * D;    // elements between consecutive tokens
+    const int kv_tok = p.Hkv * D;                 // elements between consecutive tokens
     constexpr int RPL = 1024 / Gm::ROW;           // rows covered by one 1 KB load
     constexpr int LPW = (Gm::LOADS + NQT - 1) / NQT;   // loads per wave per tile (max)
 
-    // Issue this wave's share of the direct loads of stream tile `t` into
-    // buffer `buf`.  Load u < LOADS/2 fills K rows, the rest V rows; rows
-    // past the context end repeat row L-1 (their scores are masked and their
-    // probabilities are 0, so the repeated values never contribute).
+    // Direct loads of a stream tile: this wave issues loads u = qt + i*NQT.
+    // Load u < LOADS/2 fills K rows, the rest V rows; lane `lane` of load u
+    // writes tile row r = (u % (LOADS/2))*RPL + lane/CH, slot lane%CH, with
+    // the chunk that the row's swizzle puts there.  Its byte offset from the
+    // tile's first token is loop-invariant for full tiles.
+    uint32_t loff[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+        const int u = qt + i * NQT;
+        const bool is_v = u >= Gm::LOADS / 2;
+        const int uu = is_v ? u - Gm::LOADS / 2 : u;
+        const int r = uu * RPL + lane / Gm::CH;
+        const int c = (lane % Gm::CH) ^ (is_v ? vswz<D>(r) : kswz<D>(r));
+        loff[i] = (uint32_t)(r * kv_tok + 8 * c) * 2u;
+    }
     auto issue_tile = [&](int t, int buf) {
         const int key0 = (t_begin + t) * KT;
-        const uint32_t dst = stream_lds + buf * Gm::TILE;
+        const bool partial = key0 + KT > L;
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
             const int u = qt + i * NQT;
             if (u < Gm::LOADS) {
                 const bool is_v = u >= Gm::LOADS / 2;
                 const int uu = is_v ? u - Gm::LOADS / 2 : u;
-                const int r = uu * RPL + lane / Gm::CH;    // tile row written by this lane
-                const int s = lane % Gm::CH;               // its 16-byte slot in that row
-                const int c = s ^ (is_v ? vswz<D>(r) : kswz<D>(r));
-                int key = key0 + r;
-                key = key < L ? key : L - 1;
-                const uint16_t *src = (is_v ? kv_v : kv_k) + key * kv_tok + 8 * c;
-                dma16(src, __builtin_amdgcn_readfirstlane(dst + (is_v ? Gm::KBYTES : 0) +
-                                                          uu * 1024));
+                const uint16_t *base = (is_v ? kv_v : kv_k) + (int64_t)key0 * kv_tok;
+                uint32_t off = loff[i];
+                if (partial) {
+                    // rows past the context end repeat row L-1: their scores
+                    // are masked and their probabilities are 0
+                    const int r = uu * RPL + lane / Gm::CH;
+                    const int rr = key0 + r < L ? r : L - 1 - key0;
+                    off = off - (uint32_t)((r - rr) * kv_tok) * 2u;
+                }
+                dma16_s(base, off,
+                        lds0 + stream_off + buf * Gm::TILE + (is_v ? Gm::KBYTES : 0) + uu * 1024);
             }
         }
     };
@@ -297,21 +323,44 @@ void fused_decode_attn(const Params p)
             wait_vm<0>();
     };
 
-    // Per-tile compute of a live wave.  ACCUM: p = exp2(s*c - m_ref) against
-    // the fixed reference; otherwise only the exact maxima are tracked.  The
-    // accumulators are written only by the matrix cores, on every iteration
-    // of the compute loop, so they stay in accumulation registers.
-    auto compute_tile = [&](int it, bool want_max, auto accum_tag) {
+    // Loop-invariant per-lane LDS byte offsets (stream base included), so
+    // that every fragment read is one instruction with an immediate offset.
+    // K: lane row c32, d chunk 2c+h.  V (transposing reads): lane group
+    // (h, dh) reads keys 16kc+4h+{0..3} (then +8) at d = 32db+16dh+{0..15};
+    // the row swizzle depends only on key & 3, the same for all four keys of
+    // a read, so kc and the +8 rows are immediate offsets too.
+    uint32_t koff[Gm::DC];
+#pragma unroll
+    for (int c = 0; c < Gm::DC; ++c)
+        koff[c] = stream_off + c32 * Gm::ROW + 16 * ((2 * c + h) ^ kswz<D>(c32));
+    uint32_t voff[Gm::DB];
+    {
+        const int dh = (lane >> 4) & 1;
+        const int sl = lane & 15;
+        const int key_a = 4 * h + (sl >> 2);
+#pragma unroll
+        for (int db = 0; db < Gm::DB; ++db) {
+            const int cidx = 4 * db + 2 * dh + ((sl & 3) >> 1);
+            voff[db] = stream_off + Gm::KBYTES + key_a * Gm::ROW + 16 * (cidx ^ vswz<D>(key_a)) +
+                       8 * (sl & 1);
+        }
+    }
+
+    // Per-tile compute of a live wave on LDS buffer BUF.  ACCUM: p =
+    // exp2(s*c - m_ref) against the fixed reference; otherwise only the exact
+    // maxima are tracked.  The accumulators are written only by the matrix
+    // cores, on every iteration of the compute loop, so they stay in
+    // accumulation registers.
+    auto compute_tile = [&](int it, auto buf_tag, bool want_max, auto accum_tag) {
         constexpr bool ACCUM = decltype(accum_tag)::value;
-        const char *kl = stream_ptr + (it % NBUF) * Gm::TILE;
-        const char *vl = kl + Gm::KBYTES;
+        constexpr int BUF = decltype(buf_tag)::value;
+        const char *kl = smem + BUF * Gm::TILE;
         const int kbase = (t_begin + it) * KT;
-        // S^T = K * Q^T: K fragment of lane row c32, d chunk 2c+h
+        // S^T = K * Q^T
         f32x16 s = f32x16{};
 #pragma unroll
         for (int c = 0; c < Gm::DC; ++c) {
-            const u32x4 kf = *reinterpret_cast<const u32x4 *>(
-                kl + c32 * Gm::ROW + 16 * ((2 * c + h) ^ kswz<D>(c32)));
+            const u32x4 kf = *reinterpret_cast<const u32x4 *>(kl + koff[c]);
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf),
                                                         __builtin_bit_cast(bf16x8, qf[c]), s, 0,
                                                         0, 0);
@@ -333,9 +382,8 @@ void fused_decode_attn(const Params p)
             m_ref = __builtin_fmaxf(m_ref, mx * cs);
         }
         if constexpr (ACCUM) {
-            // probabilities as bf16 B operands; the row sum adds the rounded
-            // values, so the normalisation matches the weighted sum the
-            // matrix cores form
+            // probabilities as bf16 B operands; l_run adds the rounded
+            // values, l_lse the unrounded ones
             u32x4 pb[2];
             const float nm = -m_ref;
             float sum = l_run, sum_x = l_lse;
@@ -355,23 +403,14 @@ void fused_decode_attn(const Params p)
                 }
             l_run = sum;
             l_lse = sum_x;
-            // O^T += V^T * P^T.  V^T fragments come from transposing reads
-            // of the row-major V tile: lane group (h, dh) reads keys
-            // 16kc+4h+{0..3} (then +8) at d = 32db+16dh+{0..15}
-            const int dh = (lane >> 4) & 1;
-            const int sl = lane & 15;
+            // O^T += V^T * P^T
 #pragma unroll
             for (int db = 0; db < Gm::DB; ++db)
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc) {
-                    const int key_a = 16 * kc + 4 * h + (sl >> 2);
-                    const int key_b = key_a + 8;
-                    const int cidx = 4 * db + 2 * dh + ((sl & 3) >> 1);
-                    const int boff = 8 * (sl & 1);
-                    const i16x4 va =
-                        lds_tr16(vl + key_a * Gm::ROW + 16 * (cidx ^ vswz<D>(key_a)) + boff);
-                    const i16x4 vb =
-                        lds_tr16(vl + key_b * Gm::ROW + 16 * (cidx ^ vswz<D>(key_b)) + boff);
+                    const char *va_p = kl + voff[db] + 16 * kc * Gm::ROW;
+                    const i16x4 va = lds_tr16(va_p);
+                    const i16x4 vb = lds_tr16(va_p + 8 * Gm::ROW);
                     const bf16x8 vf = __builtin_shufflevector(
                         __builtin_bit_cast(bf16x4_t, va), __builtin_bit_cast(bf16x4_t, vb), 0, 1,
                         2, 3, 4, 5, 6, 7);
@@ -383,7 +422,9 @@ void fused_decode_attn(const Params p)
 
     // One sweep over the stream's tiles with NBUF-deep direct-load
     // prefetch and one workgroup barrier per tile.  Every wave executes the
-    // same number of barriers; waves without query rows only load.
+    // same number of barriers; waves without query rows only load.  The
+    // compute loop is unrolled NBUF times so that buffer offsets are
+    // immediates.
     auto sweep = [&](bool first_max, auto accum_tag) {
 #pragma unroll
         for (int t = 0; t < NBUF - 1; ++t)
@@ -397,15 +438,188 @@ void fused_decode_attn(const Params p)
                 issue_tile(it + NBUF - 1, (it + NBUF - 1) % NBUF);
         };
         if (wave_live) {
-            for (int it = 0; it < n_mine; ++it) {
-                step(it);
-                compute_tile(it, first_max && it == 0, accum_tag);
+            int it = 0;
+            auto one = [&](auto buf_tag) {
+                if (it < n_mine) {
+                    step(it);
+                    compute_tile(it, buf_tag, first_max && it == 0, accum_tag);
+                    ++it;
+                }
+            };
+            while (it < n_mine) {
+                one(std::integral_constant<int, 0>{});
+                one(std::integral_constant<int, 1 % NBUF>{});
+                if constexpr (NBUF > 2)
+                    one(std::integral_constant<int, 2 % NBUF>{});
+                if constexpr (NBUF > 3)
+                    one(std::integral_constant<int, 3 % NBUF>{});
             }
-            for (int it = n_mine; it < iters; ++it)
+            for (; it < iters; ++it)
                 step(it);
         } else {
             for (int it = 0; it < iters; ++it)
                 step(it);
+        }
+        wait_vm<0>();
+        block_barrier();                           // buffers free for the next user
+    };
+
+    // Software-pipelined accumulation sweep.  Iteration `it` runs the softmax
+    // of tile it on the vector units while the matrix cores compute the
+    // scores of tile it+1, then P.V of tile it; so each wave keeps its VALU,
+    // MFMA and LDS work overlapped instead of alternating between them.
+    // Buffers in use in iteration it: K(it+1) and V(it); the direct loads of
+    // tile it+NBUF-1 refill the buffer of tile it-1 (NBUF >= 3).
+    auto sweep_acc = [&](bool first_max) {
+        static_assert(NBUF >= 3, "the pipelined sweep reads two tiles per iteration");
+#pragma unroll
+        for (int t = 0; t < NBUF - 1; ++t)
+            if (t < n_mine)
+                issue_tile(t, t);
+        // tile t in LDS for every wave, called at the top of iteration `cur`,
+        // when tiles 0 .. min(cur+NBUF-2, n_mine-1) have been issued
+        auto sync_tile = [&](int t, int cur) {
+            const int issued_last = (cur + NBUF - 2 < n_mine - 1) ? cur + NBUF - 2 : n_mine - 1;
+            wait_tiles(issued_last - t);
+            block_barrier();
+        };
+        if (!wave_live) {
+            sync_tile(0, 0);
+            for (int it = 0; it < iters; ++it) {
+                if (it + 1 < n_mine)
+                    sync_tile(it + 1, it);
+                else
+                    block_barrier();
+                if (it + NBUF - 1 < n_mine)
+                    issue_tile(it + NBUF - 1, (it + NBUF - 1) % NBUF);
+            }
+        } else {
+            auto kread = [&](int buf, u32x4 (&kf)[Gm::DC]) {
+                const char *kl = smem + buf * Gm::TILE;
+#pragma unroll
+                for (int c = 0; c < Gm::DC; ++c)
+                    kf[c] = *reinterpret_cast<const u32x4 *>(kl + koff[c]);
+            };
+            auto mask = [&](f32x16 &s, int it) {
+                const int kbase = (t_begin + it) * KT;
+                if (kbase + KT > L) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = kbase + 8 * (r >> 2) + 4 * h + (r & 3);
+                        if (key >= L)
+                            s[r] = NEG_INF;
+                    }
+                }
+            };
+            f32x16 s_cur = f32x16{};
+            if (n_mine > 0) {
+                sync_tile(0, 0);
+                u32x4 kf[Gm::DC];
+                kread(0, kf);
+#pragma unroll
+                for (int c = 0; c < Gm::DC; ++c)
+                    s_cur = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, kf[c]), __builtin_bit_cast(bf16x8, qf[c]),
+                        s_cur, 0, 0, 0);
+                mask(s_cur, 0);
+                if (first_max) {
+                    float mx = s_cur[0];
+#pragma unroll
+                    for (int r = 1; r < 16; ++r)
+                        mx = __builtin_fmaxf(mx, s_cur[r]);
+                    mx = __builtin_fmaxf(mx, swap32(mx, h));
+                    m_ref = __builtin_fmaxf(m_ref, mx * cs);
+                }
+            } else {
+                block_barrier();
+            }
+            // one pipelined iteration; HAS_NEXT (compile time) keeps the
+            // steady-state body free of branches around its MFMAs
+            auto body = [&](int it, auto next_tag) {
+                constexpr bool HAS_NEXT = decltype(next_tag)::value;
+                if constexpr (HAS_NEXT)
+                    sync_tile(it + 1, it);
+                else
+                    block_barrier();
+                if (it + NBUF - 1 < n_mine)
+                    issue_tile(it + NBUF - 1, (it + NBUF - 1) % NBUF);
+                const int bcur = it % NBUF, bnext = (it + 1) % NBUF;
+                // (1) all LDS fragment reads of the iteration: V^T of tile it,
+                // K of tile it+1; they land while the vector units work
+                bf16x8 vf[Gm::DB][2];
+                {
+                    const char *vl = smem + bcur * Gm::TILE;
+#pragma unroll
+                    for (int db = 0; db < Gm::DB; ++db)
+#pragma unroll
+                        for (int kc = 0; kc < 2; ++kc) {
+                            const char *va_p = vl + voff[db] + 16 * kc * Gm::ROW;
+                            const i16x4 va = lds_tr16(va_p);
+                            const i16x4 vb = lds_tr16(va_p + 8 * Gm::ROW);
+                            vf[db][kc] = __builtin_shufflevector(
+                                __builtin_bit_cast(bf16x4_t, va), __builtin_bit_cast(bf16x4_t, vb),
+                                0, 1, 2, 3, 4, 5, 6, 7);
+                        }
+                }
+                u32x4 kf[Gm::DC];
+                if constexpr (HAS_NEXT)
+                    kread(bnext, kf);
+                __builtin_amdgcn_sched_barrier(0);
+                // (2) softmax of tile it on the vector units: bf16 B operands,
+                // l_run adds the rounded values, l_lse the unrounded ones
+                u32x4 pb[2];
+                {
+                    const float nm = -m_ref;
+                    float sum = l_run, sum_x = l_lse;
+#pragma unroll
+                    for (int e2 = 0; e2 < 8; ++e2) {
+                        const int r = 2 * e2;
+                        const float p0 = exp2_fast(__builtin_fmaf(s_cur[r], cs, nm));
+                        const float p1 = exp2_fast(__builtin_fmaf(s_cur[r + 1], cs, nm));
+                        const uint32_t pk = pack_bf16(p0, p1);
+                        pb[e2 >> 2][e2 & 3] = pk;
+                        sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
+                                                              __builtin_bit_cast(bf16x2, BF16_ONES),
+                                                              sum, false);
+                        sum_x += p0 + p1;
+                    }
+                    l_run = sum;
+                    l_lse = sum_x;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                // (3) matrix cores: O^T += V^T * P^T for tile it, then the
+                // scores of tile it+1
+#pragma unroll
+                for (int db = 0; db < Gm::DB; ++db)
+#pragma unroll
+                    for (int kc = 0; kc < 2; ++kc)
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            vf[db][kc], __builtin_bit_cast(bf16x8, pb[kc]), acc[db], 0, 0, 0);
+                f32x16 s_next = f32x16{};
+                if constexpr (HAS_NEXT) {
+#pragma unroll
+                    for (int c = 0; c < Gm::DC; ++c)
+                        s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, kf[c]), __builtin_bit_cast(bf16x8, qf[c]),
+                            s_next, 0, 0, 0);
+                }
+                if constexpr (HAS_NEXT) {
+                    mask(s_next, it + 1);
+                    s_cur = s_next;
+                }
+            };
+            int it = 0;
+            for (; it + 1 < n_mine; ++it)
+                body(it, std::true_type{});
+            if (it < n_mine) {
+                body(it, std::false_type{});
+                ++it;
+            }
+            for (int it = n_mine; it < iters; ++it) {
+                block_barrier();
+                if (it + NBUF - 1 < n_mine)
+                    issue_tile(it + NBUF - 1, (it + NBUF - 1) % NBUF);
+            }
         }
         wait_vm<0>();
         block_barrier();                           // buffers free for the next user
@@ -417,7 +631,7 @@ void fused_decode_attn(const Params p)
     // normalisation is exact.  Otherwise (scores rising by more than ~44
     // nats along the context) the workgroup sweeps again: exact maxima
     // first, then the accumulation against them.
-    sweep(true, std::true_type{});
+    sweep_acc(true);
     if (__syncthreads_or(qvalid && !(l_lse < SAFE_SUM))) {
         m_ref = NEG_INF;
         l_run = 0.f;
@@ -426,7 +640,7 @@ void fused_decode_attn(const Params p)
         for (int db = 0; db < Gm::DB; ++db)
             acc[db] = f32x16{};
         sweep(true, std::false_type{});
-        sweep(false, std::true_type{});
+        sweep_acc(false);
     }
 
     // The vector-unit stages below work on a copy of the accumulators pinned
