@@ -220,20 +220,22 @@ def measure(cfg: int, steps: int, warmup: int):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    # timed region: K steps; every launch is bracketed by events recorded on
-    # the stream it is enqueued on, so the kernel's own duration comes from
-    # the same run as the wall-clock rate
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    # timed region: K back-to-back steps (one launch each), bracketed by
+    # events recorded on the launch stream; the average launch duration is
+    # their elapsed time / K, so the rate and the kernel duration come from
+    # the same run.  No per-launch events, so the host never starves the GPU.
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(steps):
-        ev[i][0].record(stream)
         step(i)
-        ev[i][1].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / steps
-    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    launch_ms = ev0.elapsed_time(ev1) / steps
 
     # spot check of a few rows against the oracle (not timed)
     from oracle import oracle as O
