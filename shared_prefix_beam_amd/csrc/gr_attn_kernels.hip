@@ -279,31 +279,44 @@ void fused_decode_attn(const Params p)
         const int c = (lane % Gm::CH) ^ (is_v ? vswz<D>(r) : kswz<D>(r));
         loff[i] = (uint32_t)(r * kv_tok + 8 * c) * 2u;
     }
+    // Every load index u < LOADS when NQT divides LOADS (all configurations
+    // but the guard keeps other shapes correct).
+    constexpr bool EVEN = Gm::LOADS % NQT == 0;
     auto issue_tile = [&](int t, int buf) {
         const int key0 = (t_begin + t) * KT;
-        const bool partial = key0 + KT > L;
+        const uint32_t dst0 = lds0 + stream_off + buf * Gm::TILE;
+        if (key0 + KT <= L) {
+            // full tile: loop-invariant offsets, no per-lane arithmetic
 #pragma unroll
-        for (int i = 0; i < LPW; ++i) {
-            const int u = qt + i * NQT;
-            if (u < Gm::LOADS) {
-                const bool is_v = u >= Gm::LOADS / 2;
-                const int uu = is_v ? u - Gm::LOADS / 2 : u;
-                const uint16_t *base = (is_v ? kv_v : kv_k) + (int64_t)key0 * kv_tok;
-                uint32_t off = loff[i];
-                if (partial) {
-                    // rows past the context end repeat row L-1: their scores
-                    // are masked and their probabilities are 0
+            for (int i = 0; i < LPW; ++i) {
+                const int u = qt + i * NQT;
+                if (EVEN || u < Gm::LOADS) {
+                    const bool is_v = u >= Gm::LOADS / 2;
+                    const int uu = is_v ? u - Gm::LOADS / 2 : u;
+                    dma16_s((is_v ? kv_v : kv_k) + (int64_t)key0 * kv_tok, loff[i],
+                            dst0 + (is_v ? Gm::KBYTES : 0) + uu * 1024);
+                }
+            }
+        } else {
+            // the context's last, partial tile: rows past the end repeat row
+            // L-1 (their scores are masked and their probabilities are 0)
+#pragma unroll
+            for (int i = 0; i < LPW; ++i) {
+                const int u = qt + i * NQT;
+                if (EVEN || u < Gm::LOADS) {
+                    const bool is_v = u >= Gm::LOADS / 2;
+                    const int uu = is_v ? u - Gm::LOADS / 2 : u;
                     const int r = uu * RPL + lane / Gm::CH;
                     const int rr = key0 + r < L ? r : L - 1 - key0;
-                    off = off - (uint32_t)((r - rr) * kv_tok) * 2u;
+                    const uint32_t off = loff[i] - (uint32_t)((r - rr) * kv_tok) * 2u;
+                    dma16_s((is_v ? kv_v : kv_k) + (int64_t)key0 * kv_tok, off,
+                            dst0 + (is_v ? Gm::KBYTES : 0) + uu * 1024);
                 }
-                dma16_s(base, off,
-                        lds0 + stream_off + buf * Gm::TILE + (is_v ? Gm::KBYTES : 0) + uu * 1024);
             }
         }
     };
     // loads this wave issues per tile (waves of a stream share LOADS)
-    const int my_loads = (Gm::LOADS - qt + NQT - 1) / NQT;
+    const int my_loads = EVEN ? Gm::LOADS / NQT : (Gm::LOADS - qt + NQT - 1) / NQT;
     // wait until at most `pending` later tiles of this wave are still loading
     auto wait_tiles = [&](int pending) {
         const int n = pending > 0 ? pending * my_loads : 0;
@@ -479,8 +492,10 @@ void fused_decode_attn(const Params p)
         // tile t in LDS for every wave, called at the top of iteration `cur`,
         // when tiles 0 .. min(cur+NBUF-2, n_mine-1) have been issued
         auto sync_tile = [&](int t, int cur) {
-            const int issued_last = (cur + NBUF - 2 < n_mine - 1) ? cur + NBUF - 2 : n_mine - 1;
-            wait_tiles(issued_last - t);
+            if (EVEN && t == cur + 1 && cur + NBUF - 2 < n_mine - 1)
+                wait_vm<(NBUF - 3) * (Gm::LOADS / NQT)>();   // steady state
+            else
+                wait_tiles(((cur + NBUF - 2 < n_mine - 1) ? cur + NBUF - 2 : n_mine - 1) - t);
             block_barrier();
         };
         if (!wave_live) {
@@ -566,7 +581,10 @@ void fused_decode_attn(const Params p)
                     kread(bnext, kf);
                 __builtin_amdgcn_sched_barrier(0);
                 // (2) softmax of tile it on the vector units: bf16 B operands,
-                // l_run adds the rounded values, l_lse the unrounded ones
+                // l_run adds the rounded values, l_lse the unrounded ones.
+                // Only a stream's last tile can hold keys past the context end.
+                if constexpr (!HAS_NEXT)
+                    mask(s_cur, it);
                 u32x4 pb[2];
                 {
                     const float nm = -m_ref;
@@ -603,10 +621,8 @@ void fused_decode_attn(const Params p)
                             __builtin_bit_cast(bf16x8, kf[c]), __builtin_bit_cast(bf16x8, qf[c]),
                             s_next, 0, 0, 0);
                 }
-                if constexpr (HAS_NEXT) {
-                    mask(s_next, it + 1);
+                if constexpr (HAS_NEXT)
                     s_cur = s_next;
-                }
             };
             int it = 0;
             for (; it + 1 < n_mine; ++it)

@@ -67,6 +67,25 @@ def test_small_shapes_all_rows(case, which):
     assert_parity(out, lse, ref_out, ref_lse, f"{name}/{which}")
 
 
+TILINGS = [(128, 8, 1), (128, 4, 1), (128, 4, 2), (128, 2, 2), (64, 4, 1), (64, 2, 2), (64, 2, 4)]
+
+
+@pytest.mark.parametrize("tiling", TILINGS, ids=[f"d{d}_q{a}_k{c}" for d, a, c in TILINGS])
+def test_every_tiling_ragged(tiling, monkeypatch):
+    """Each compiled (query tile, key streams) shape, forced through the
+    planner override, on ragged requests: partial context tiles, partial
+    query tiles, streams with unequal tile counts and an empty stream."""
+    D, nqt, nks = tiling
+    monkeypatch.setenv("GR_ATTN_TILE", f"{nqt},{nks}")
+    Hq, Hkv = (16, 8) if D == 128 else (8, 4)
+    inp = I.custom(B=3, Hq=Hq, Hkv=Hkv, D=D, W=[37, 5, 130], ctx_len=[1000, 33, 517],
+                   beam_len=[3, 1, 5], seed=100 + nqt * 10 + nks)
+    log(f"[parity] tiling D={D} NQT={nqt} NKS={nks} R={inp.R}")
+    out, lse = run_lib(inp, "fused")
+    ref_out, ref_lse = O.decode_attn_inputs(inp)
+    assert_parity(out, lse, ref_out, ref_lse, f"tiling {tiling}")
+
+
 def test_rising_scores_take_exact_sweep():
     """Scores that grow by far more than 44 nats along the context: the
     fixed first-tile reference would overflow, so the exact sweep must run."""
