@@ -51,6 +51,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int KT = 32;          // keys per context tile
+constexpr int PSTEPS = 4;       // beam steps gathered into LDS at a time, at most
 constexpr float SAFE_SUM = 1.8446744e19f;  // 2^64: largest row sum accepted in pass 0
 constexpr float NEG_INF = -__builtin_huge_valf();
 constexpr uint32_t BF16_ONES = 0x3f803f80u;  // two bf16 ones
@@ -670,37 +671,129 @@ void fused_decode_attn(const Params p)
     }
 
     // ---- per-beam stage: BeamKV steps ks, ks+NKS, ... along BeamPath ------
-    if (wave_live) {
-        for (int s = ks; s < T; s += NKS) {
-            const int idx = qvalid ? p.beam_path[(int64_t)qrow * p.T_cap + s] : 0;
+    // Each lane folds the K and V rows of its query's path token for a step
+    // into its (max, sums, O) online.  When G divides 32 the 32/G beams of a
+    // wave are gathered first into the (now free) tile buffers with direct
+    // loads, each covering whole rows (a 1 KB load takes 1024/ROW rows: few
+    // cache lines per instruction), up to `sch` steps at a time; row beta's
+    // 16-byte chunks sit at slot chunk ^ (beta & (CH-1)).  The path entry of
+    // beam beta is the one lane beta*G fetched with Q.  Otherwise each lane
+    // loads its rows from memory.
+    const int n_steps = T > ks ? (T - ks + NKS - 1) / NKS : 0;
+    auto step_idx = [&](int i) __attribute__((always_inline)) {
+        return qvalid ? p.beam_path[(int64_t)qrow * p.T_cap + ks + i * NKS] : 0;
+    };
+    auto fold = [&](const u32x4 (&kr)[Gm::DC], const u32x2 (&vr)[Gm::DB][4])
+                    __attribute__((always_inline)) {
+        float dot = 0.f;
+#pragma unroll
+        for (int c = 0; c < Gm::DC; ++c)
+            dot = dot8(qf[c], kr[c], dot);
+        dot += swap32(dot, h);
+        const float tz = dot * cs;
+        const float mn = __builtin_fmaxf(m_ref, tz);
+        const float alpha = exp2_fast(m_ref - mn);
+        const float pw = exp2_fast(tz - mn);
+        m_ref = mn;
+        l_run = l_run * alpha + (h == 0 ? pw : 0.f);
+        l_lse = l_lse * alpha + (h == 0 ? pw : 0.f);
+#pragma unroll
+        for (int db = 0; db < Gm::DB; ++db)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const u32x2 v = vr[db][rg];
+                f32x16 &ov = o[db];
+                ov[4 * rg + 0] = ov[4 * rg + 0] * alpha + pw * bf16lo(v[0]);
+                ov[4 * rg + 1] = ov[4 * rg + 1] * alpha + pw * bf16hi(v[0]);
+                ov[4 * rg + 2] = ov[4 * rg + 2] * alpha + pw * bf16lo(v[1]);
+                ov[4 * rg + 3] = ov[4 * rg + 3] * alpha + pw * bf16hi(v[1]);
+            }
+    };
+    constexpr int RING = NKS * NBUF * Gm::TILE;
+    const int nb = 32 / G;                         // beams of a wave (G divides 32)
+    const int sb = 2 * nb * Gm::ROW;               // LDS bytes per gathered step
+    const int fit = RING / (NQT * NKS * sb);
+    const int sch = (32 % G == 0) ? (fit < PSTEPS ? fit : PSTEPS) : 0;
+    if (wave_live && sch > 0) {
+        const uint32_t area = lds0 + wave * sch * sb;
+        const char *area_p = smem + wave * sch * sb;
+        const int lpr = nb * Gm::ROW / 1024;       // 1 KB loads per step for K (and V)
+        const int beta_l = lane / Gm::CH;
+        const int beta_q = c32 / G;                // this lane's beam within the wave
+        const int sw = beta_q & (Gm::CH - 1);
+        const uint16_t *bk = p.beam_k + ((int64_t)b * p.beam_cap * p.Hkv + g) * D;
+        const uint16_t *bv = p.beam_v + ((int64_t)b * p.beam_cap * p.Hkv + g) * D;
+        constexpr int MAXL = 32 * Gm::ROW / 1024;  // 1 KB loads per step at G = 1
+        for (int s0 = 0; s0 < n_steps; s0 += sch) {
+            const int cnt = sch < n_steps - s0 ? sch : n_steps - s0;
+            // path entries of the chunk's steps: one load per lane and step,
+            // then the shuffles to the rows each lane's direct loads cover,
+            // all before the first direct load
+            int myidx[PSTEPS];
+#pragma unroll
+            for (int i = 0; i < PSTEPS; ++i)
+                myidx[i] = i < cnt ? step_idx(s0 + i) : 0;
+            int rid[PSTEPS][MAXL];
+#pragma unroll
+            for (int i = 0; i < PSTEPS; ++i)
+#pragma unroll
+                for (int u = 0; u < MAXL; ++u) {
+                    const int beta = u * (1024 / Gm::ROW) + beta_l;
+                    rid[i][u] = (i < cnt && u < lpr) ? __shfl(myidx[i], beta * G) : 0;
+                }
+#pragma unroll
+            for (int i = 0; i < PSTEPS; ++i)
+#pragma unroll
+                for (int u = 0; u < MAXL; ++u)
+                    if (i < cnt && u < lpr) {
+                        const int beta = u * (1024 / Gm::ROW) + beta_l;
+                        const int64_t src = (int64_t)rid[i][u] * p.Hkv * D +
+                                            8 * ((lane % Gm::CH) ^ (beta & (Gm::CH - 1)));
+                        const uint32_t dst = area + i * sb + u * 1024;
+                        dma16(bk + src, dst);
+                        dma16(bv + src, dst + nb * Gm::ROW);
+                    }
+            wait_vm<0>();
+            for (int i = 0; i < cnt; ++i) {
+                const char *krow = area_p + i * sb + beta_q * Gm::ROW;
+                const char *vrow = krow + nb * Gm::ROW;
+                u32x4 kr[Gm::DC];
+                u32x2 vr[Gm::DB][4];
+#pragma unroll
+                for (int c = 0; c < Gm::DC; ++c)
+                    kr[c] = *reinterpret_cast<const u32x4 *>(krow + 16 * ((2 * c + h) ^ sw));
+#pragma unroll
+                for (int db = 0; db < Gm::DB; ++db)
+#pragma unroll
+                    for (int rg = 0; rg < 4; ++rg)
+                        vr[db][rg] = *reinterpret_cast<const u32x2 *>(
+                            vrow + 16 * ((4 * db + rg) ^ sw) + 8 * h);
+                fold(kr, vr);
+            }
+            // this wave's reads of the area are done before it is refilled
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+    } else if (wave_live) {
+        for (int i = 0; i < n_steps; ++i) {
+            const int idx = step_idx(i);
             const int64_t base = (((int64_t)b * p.beam_cap + idx) * p.Hkv + g) * D;
-            const uint16_t *kr = p.beam_k + base + 8 * h;
-            float dot = 0.f;
+            const uint16_t *kp = p.beam_k + base + 8 * h;
+            const uint16_t *vp = p.beam_v + base + 4 * h;
+            u32x4 kr[Gm::DC];
+            u32x2 vr[Gm::DB][4];
 #pragma unroll
             for (int c = 0; c < Gm::DC; ++c)
-                dot = dot8(qf[c], qvalid ? ldg16(kr + 16 * c) : u32x4{0, 0, 0, 0}, dot);
-            dot += swap32(dot, h);
-            const float tz = dot * cs;
-            const float mn = __builtin_fmaxf(m_ref, tz);
-            const float alpha = exp2_fast(m_ref - mn);
-            const float pw = exp2_fast(tz - mn);
-            m_ref = mn;
-            l_run = l_run * alpha + (h == 0 ? pw : 0.f);
-            l_lse = l_lse * alpha + (h == 0 ? pw : 0.f);
-            const uint16_t *vr = p.beam_v + base + 4 * h;
+                kr[c] = qvalid ? ldg16(kp + 16 * c) : u32x4{0, 0, 0, 0};
 #pragma unroll
             for (int db = 0; db < Gm::DB; ++db)
 #pragma unroll
-                for (int rg = 0; rg < 4; ++rg) {
-                    const u32x2 v = qvalid ? ldg8(vr + 32 * db + 8 * rg) : u32x2{0, 0};
-                    f32x16 &ov = o[db];
-                    ov[4 * rg + 0] = ov[4 * rg + 0] * alpha + pw * bf16lo(v[0]);
-                    ov[4 * rg + 1] = ov[4 * rg + 1] * alpha + pw * bf16hi(v[0]);
-                    ov[4 * rg + 2] = ov[4 * rg + 2] * alpha + pw * bf16lo(v[1]);
-                    ov[4 * rg + 3] = ov[4 * rg + 3] * alpha + pw * bf16hi(v[1]);
-                }
+                for (int rg = 0; rg < 4; ++rg)
+                    vr[db][rg] = qvalid ? ldg8(vp + 32 * db + 8 * rg) : u32x2{0, 0};
+            fold(kr, vr);
         }
     }
+    if constexpr (NKS > 1)
+        block_barrier();                           // gathered rows read before the merge
     // full row sums (the two lane halves held different keys)
     l_run += swap32(l_run, h);
     l_lse += swap32(l_lse, h);
