@@ -681,7 +681,9 @@ void fused_decode_attn(const Params p)
     // loads its rows from memory.
     const int n_steps = T > ks ? (T - ks + NKS - 1) / NKS : 0;
     auto step_idx = [&](int i) __attribute__((always_inline)) {
-        return qvalid ? p.beam_path[(int64_t)qrow * p.T_cap + ks + i * NKS] : 0;
+        int qr = qrow;
+        asm volatile("" : "+v"(qr));
+        return qvalid ? p.beam_path[(int64_t)qr * p.T_cap + ks + i * NKS] : 0;
     };
     auto fold = [&](const u32x4 (&kr)[Gm::DC], const u32x2 (&vr)[Gm::DB][4])
                     __attribute__((always_inline)) {
@@ -849,7 +851,11 @@ void fused_decode_attn(const Params p)
 
     // ---- epilogue: normalise, bf16 output, fp32 natural-log LSE ----------
     if (ks == 0 && wave_live && qvalid) {
-        const int64_t orow = (int64_t)qrow * p.Hq + qhead;
+        // recomputed here from opaque copies: the 64-bit row offset of the Q
+        // load would otherwise be kept (and spilled) across the context loop
+        int qr = qrow, qh = qhead;
+        asm volatile("" : "+v"(qr), "+v"(qh));
+        const int64_t orow = (int64_t)qr * p.Hq + qh;
         const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
         uint16_t *dst = p.out + orow * D + 4 * h;
 #pragma unroll
