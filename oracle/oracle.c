@@ -208,3 +208,71 @@ int oracle_decode_attn(int B, int R, int Hq, int Hkv, int D, int T_cap,
     free(tid);
     return status;
 }
+
+/*
+ * One decode step of the per-beam state: BeamKV append and BeamPath update.
+ *
+ * Data model (GR-Inference blog, section on system design: BeamKV holds the
+ * short per-beam history and BeamPath records how beams fork and reorder by
+ * index, so the long context is never copied; SID-GR README, "Design
+ * Highlights": BeamPath keeps the logical parent-child relation; xGR review,
+ * section "xAttention": the unshared cache is managed per token and reached
+ * by direct index, with no block copies).
+ *
+ * Request b had W_old = row_offset_old[b+1] - row_offset_old[b] beams whose
+ * paths hold s = beam_len_old[b] tokens.  Beam selection gave it W_new =
+ * row_offset_new[b+1] - row_offset_new[b] new beams; new beam k (packed row
+ * r = row_offset_new[b] + k) descends from old beam parent[r] and its current
+ * token is step s.  Then
+ *   path_new[r][t]            = path_old[row_offset_old[b] + parent[r]][t],  t < s
+ *   path_new[r][s]            = s * W_cap + k          (its own step-s slot)
+ *   beam_k[b][s*W_cap + k][:] = new_k[r][:]            (all KV heads; same for V)
+ *   beam_len_new[b]           = s + 1  if W_new > 0, else s
+ * Path entries t > s of path_new and every other BeamKV slot are left as
+ * they are.  The paths are rebuilt into a second table (path_new must not
+ * be path_old): each new row reads only its parent's old row, so the update
+ * has no read-before-write order to respect.
+ *
+ * A row whose slot or parent is out of range (s >= T_cap, k >= W_cap,
+ * s*W_cap + k >= beam_cap, or s > 0 with parent outside [0, W_old)) writes
+ * nothing; the return value counts such rows (>= 0), or is -1 on bad
+ * arguments.  Plain loops; the data are copied as raw bits.
+ */
+int oracle_beam_step(int B, int Hkv, int D, int T_cap, int W_cap, int64_t beam_cap,
+                     const int32_t *row_offset_old, const int32_t *row_offset_new,
+                     const int32_t *parent, const int32_t *path_old,
+                     const int32_t *beam_len_old, const uint16_t *new_k,
+                     const uint16_t *new_v, int32_t *path_new, int32_t *beam_len_new,
+                     uint16_t *beam_k, uint16_t *beam_v)
+{
+    if (B < 0 || Hkv <= 0 || D <= 0 || T_cap < 0 || W_cap < 0 || beam_cap < 0 ||
+        !row_offset_old || !row_offset_new || !beam_len_old || !beam_len_new)
+        return -1;
+    const int64_t row_elems = (int64_t)Hkv * D;      /* one token, all KV heads */
+    int skipped = 0;
+    for (int b = 0; b < B; ++b) {
+        const int s = beam_len_old[b];
+        const int w_old = row_offset_old[b + 1] - row_offset_old[b];
+        const int w_new = row_offset_new[b + 1] - row_offset_new[b];
+        for (int k = 0; k < w_new; ++k) {
+            const int r = row_offset_new[b] + k;
+            const int64_t slot = (int64_t)s * W_cap + k;
+            const int p = s > 0 ? parent[r] : 0;
+            if (s < 0 || s >= T_cap || k >= W_cap || slot >= beam_cap ||
+                (s > 0 && (p < 0 || p >= w_old))) {
+                ++skipped;
+                continue;
+            }
+            for (int t = 0; t < s; ++t)
+                path_new[(int64_t)r * T_cap + t] =
+                    path_old[(int64_t)(row_offset_old[b] + p) * T_cap + t];
+            path_new[(int64_t)r * T_cap + s] = (int32_t)slot;
+            for (int64_t e = 0; e < row_elems; ++e) {
+                beam_k[((int64_t)b * beam_cap + slot) * row_elems + e] = new_k[(int64_t)r * row_elems + e];
+                beam_v[((int64_t)b * beam_cap + slot) * row_elems + e] = new_v[(int64_t)r * row_elems + e];
+            }
+        }
+        beam_len_new[b] = w_new > 0 ? s + 1 : s;
+    }
+    return skipped;
+}

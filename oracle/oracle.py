@@ -51,6 +51,9 @@ def _open(path: str):
                                        ctypes.c_double, P, P, P, P, P, P, P, P, P,
                                        P, i32, P, P, i32]
     lib.oracle_decode_attn.restype = i32
+    lib.oracle_beam_step.argtypes = [i32, i32, i32, i32, i32, i64, P, P, P, P, P, P, P, P, P,
+                                     P, P]
+    lib.oracle_beam_step.restype = i32
     return lib
 
 
@@ -133,3 +136,50 @@ def decode_attn_inputs(inp, rows=None, n_threads=None):
     return decode_attn(inp.q, inp.ctx_k, inp.ctx_v, inp.ctx_len, inp.beam_k, inp.beam_v,
                        inp.beam_path, inp.beam_len, inp.row_offset, scale=inp.scale,
                        rows=rows, n_threads=n_threads)
+
+
+def beam_step(row_offset_old, row_offset_new, parent, path_old, beam_len_old, new_k, new_v,
+              path_new, beam_k, beam_v, W_cap: int, lib=None):
+    """BeamKV append + BeamPath update of one decode step (see ``oracle_beam_step``).
+
+    ``path_new`` [R_new][T_cap] int32, ``beam_k``/``beam_v`` [B][beam_cap][Hkv][D]
+    uint16 are the state before the step; copies are updated and returned as
+    (path_new, beam_len_new, beam_k, beam_v, n_skipped_rows).
+    """
+    lib = _load() if lib is None else lib
+    row_offset_old = np.ascontiguousarray(row_offset_old, dtype=np.int32)
+    row_offset_new = np.ascontiguousarray(row_offset_new, dtype=np.int32)
+    parent = np.ascontiguousarray(parent, dtype=np.int32)
+    path_old = np.ascontiguousarray(path_old, dtype=np.int32)
+    beam_len_old = np.ascontiguousarray(beam_len_old, dtype=np.int32)
+    new_k = np.ascontiguousarray(new_k, dtype=np.uint16)
+    new_v = np.ascontiguousarray(new_v, dtype=np.uint16)
+    path_new = np.array(path_new, dtype=np.int32, copy=True)
+    beam_k = np.array(beam_k, dtype=np.uint16, copy=True)
+    beam_v = np.array(beam_v, dtype=np.uint16, copy=True)
+    B = row_offset_new.size - 1
+    assert row_offset_old.size == B + 1 and beam_len_old.size == B
+    B2, beam_cap, Hkv, D = beam_k.shape
+    assert B2 == B and beam_v.shape == beam_k.shape
+    R_new = int(row_offset_new[-1])
+    T_cap = path_new.shape[1]
+    assert path_new.shape[0] == R_new and parent.size >= R_new
+    assert path_old.ndim == 2 and path_old.shape[1] == T_cap
+    assert new_k.shape == (R_new, Hkv, D) and new_v.shape == new_k.shape
+    len_new = np.zeros(B, dtype=np.int32)
+    st = lib.oracle_beam_step(B, Hkv, D, T_cap, int(W_cap), beam_cap, _ptr(row_offset_old),
+                              _ptr(row_offset_new), _ptr(parent), _ptr(path_old),
+                              _ptr(beam_len_old), _ptr(new_k), _ptr(new_v), _ptr(path_new),
+                              _ptr(len_new), _ptr(beam_k), _ptr(beam_v))
+    if st < 0:
+        raise RuntimeError(f"oracle_beam_step failed with status {st}")
+    return path_new, len_new, beam_k, beam_v, int(st)
+
+
+def beam_step_from_library(path: str):
+    """``beam_step`` bound to another build of oracle.c (broken copies in tests)."""
+    lib = _open(path)
+
+    def fn(*args, **kw):
+        return beam_step(*args, lib=lib, **kw)
+    return fn

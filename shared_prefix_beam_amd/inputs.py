@@ -191,7 +191,7 @@ def generate(wl: Workload, seed: Optional[int] = None) -> Inputs:
 def custom(B: int, Hq: int, Hkv: int, D: int, W: Sequence[int], ctx_len: Sequence[int],
            beam_len: Sequence[int], seed: int, ctx_cap: Optional[int] = None,
            T_cap: Optional[int] = None, q_std: float = 1.0, grow_steps: bool = False,
-           dup_frac: float = 0.0) -> Inputs:
+           dup_frac: float = 0.0, W_cap: Optional[int] = None) -> Inputs:
     """Inputs with explicit per-request lengths (edge cases, small parity shapes)."""
     ctx_len = np.asarray(ctx_len, dtype=np.int32)
     beam_len = np.asarray(beam_len, dtype=np.int32)
@@ -200,11 +200,12 @@ def custom(B: int, Hq: int, Hkv: int, D: int, W: Sequence[int], ctx_len: Sequenc
     wl = Workload(f"custom_s{seed}", B=B, Hq=Hq, Hkv=Hkv, D=D, W=tuple(W),
                   ctx=("fixed", ctx_cap), T=("fixed", T_cap), seed=seed, q_std=q_std,
                   grow_steps=grow_steps, dup_frac=dup_frac)
-    return _build(np.random.default_rng(seed), wl, ctx_len, beam_len, ctx_cap, T_cap)
+    return _build(np.random.default_rng(seed), wl, ctx_len, beam_len, ctx_cap, T_cap, W_cap)
 
 
 def _build(rng: np.random.Generator, wl: Workload, ctx_len: np.ndarray,
-           beam_len: np.ndarray, ctx_cap: int, T_cap: int) -> Inputs:
+           beam_len: np.ndarray, ctx_cap: int, T_cap: int,
+           W_cap: Optional[int] = None) -> Inputs:
     B, Hq, Hkv, D = wl.B, wl.Hq, wl.Hkv, wl.D
     assert Hq % Hkv == 0 and len(wl.W) == B
     assert int(ctx_len.max(initial=0)) <= ctx_cap and int(beam_len.max(initial=0)) <= T_cap
@@ -212,7 +213,8 @@ def _build(rng: np.random.Generator, wl: Workload, ctx_len: np.ndarray,
     row_offset = np.zeros(B + 1, dtype=np.int32)
     row_offset[1:] = np.cumsum(W)
     R = int(row_offset[-1])
-    W_cap = max(int(W.max()), 1)
+    W_cap = max(int(W.max(initial=0)), 1) if W_cap is None else int(W_cap)
+    assert W_cap >= int(W.max(initial=0))
     beam_cap = T_cap * W_cap + 1          # + one always-padding slot
     pad_slot = T_cap * W_cap
 
@@ -273,6 +275,77 @@ def _build(rng: np.random.Generator, wl: Workload, ctx_len: np.ndarray,
                   beam_len=np.asarray(beam_len, dtype=np.int32), row_offset=row_offset,
                   beam_path=beam_path, widths=widths, parents=parents,
                   dup_src=dup_src, dup_rows=dup_rows, W_cap=W_cap, T_cap=T_cap)
+
+
+@dataclasses.dataclass
+class StepInputs:
+    """One BeamKV-append + BeamPath-update call and the state it applies to.
+
+    ``state`` holds the previous step's rows (``state.row_offset``), their
+    paths of ``state.beam_len[b]`` tokens and the BeamKV caches, with room for
+    one more step.  Beam selection produced ``row_offset_new`` new rows; new
+    row r descends from old beam ``parent[r]`` of its request, and its
+    current token's K/V (all KV heads) are ``new_k[r]``, ``new_v[r]``.
+    """
+
+    state: Inputs
+    row_offset_new: np.ndarray  # [B+1] i32
+    parent: np.ndarray          # [R_new] i32, in [0, W_old_b) (0 where the paths are empty)
+    new_k: np.ndarray           # [R_new][Hkv][D] u16
+    new_v: np.ndarray
+
+    @property
+    def R_new(self) -> int:
+        return int(self.row_offset_new[-1])
+
+    def digest(self) -> str:
+        h = hashlib.sha256(self.state.digest().encode())
+        for a in (self.row_offset_new, self.parent, self.new_k, self.new_v):
+            h.update(np.ascontiguousarray(a).tobytes())
+        return h.hexdigest()
+
+
+def step_inputs(B: int, Hkv: int, D: int, W_old: Sequence[int], W_new: Sequence[int],
+                beam_len: Sequence[int], seed: int, T_cap: Optional[int] = None,
+                W_cap: Optional[int] = None, Hq: Optional[int] = None) -> StepInputs:
+    """A seeded beam-step call.  The state is drawn as ``custom`` draws a
+    call (context of one token, which the step does not read), with T_cap at
+    least beam_len + 1 and W_cap at least every width; then parents (uniform
+    over the request's old beams) and the new K/V rows, in that order."""
+    beam_len = np.asarray(beam_len, dtype=np.int32)
+    T_cap = int(beam_len.max(initial=0)) + 1 if T_cap is None else T_cap
+    W_cap = max(max(W_old, default=1), max(W_new, default=1), 1) if W_cap is None else W_cap
+    state = custom(B=B, Hq=Hkv if Hq is None else Hq, Hkv=Hkv, D=D, W=W_old,
+                   ctx_len=[1] * B, beam_len=beam_len, seed=seed, T_cap=T_cap, W_cap=W_cap)
+    rng = np.random.default_rng(seed + 7919)
+    row_offset_new = np.zeros(B + 1, dtype=np.int32)
+    row_offset_new[1:] = np.cumsum(np.asarray(W_new, dtype=np.int64))
+    parent = np.zeros(int(row_offset_new[-1]), dtype=np.int32)
+    for b in range(B):
+        n = int(W_new[b])
+        if n and int(beam_len[b]) > 0 and int(W_old[b]) > 0:
+            parent[row_offset_new[b]:row_offset_new[b + 1]] = rng.integers(0, int(W_old[b]), size=n)
+    R_new = int(row_offset_new[-1])
+    new_k = _normal_bf16(rng, (R_new, Hkv, D), 1.0)
+    new_v = _normal_bf16(rng, (R_new, Hkv, D), 1.0)
+    return StepInputs(state=state, row_offset_new=row_offset_new, parent=parent,
+                      new_k=new_k, new_v=new_v)
+
+
+# Beam-step calls at the attention workloads' shapes: the step that appends
+# token 3 to every request of the W=128 and W=900 workloads.
+STEP_WORKLOADS = {
+    2: dict(name="qwen3_0.6b_b8_w128_step3", B=8, Hkv=8, D=128, W_old=(128,) * 8,
+            W_new=(128,) * 8, beam_len=(3,) * 8, seed=2202),
+    4: dict(name="qwen3_0.6b_b4_w900_step3", B=4, Hkv=8, D=128, W_old=(900,) * 4,
+            W_new=(900,) * 4, beam_len=(3,) * 4, seed=4404),
+}
+
+
+def step_workload(cfg: int) -> StepInputs:
+    w = dict(STEP_WORKLOADS[cfg])
+    w.pop("name")
+    return step_inputs(**w)
 
 
 def unique_beam_rows(inp: Inputs) -> List[int]:
