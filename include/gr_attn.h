@@ -121,6 +121,66 @@ int gr_check_metadata(const gr_decode_attn_dims *dims, const int32_t *row_offset
                       const int32_t *ctx_len, const int32_t *beam_path,
                       const int32_t *beam_len, int32_t *violations, void *stream);
 
+/* Sizes of one beam step.  Host memory; read only during the call. */
+typedef struct gr_beam_step_dims {
+    int32_t B;        /* requests (>= 0) */
+    int32_t R_old;    /* rows before the step = row_offset_old[B] (>= 0) */
+    int32_t R_new;    /* rows after beam selection = row_offset_new[B] (>= 0) */
+    int32_t Hkv;      /* KV heads (>= 1) */
+    int32_t D;        /* head dim: 64 or 128 */
+    int32_t T_cap;    /* row stride of both BeamPath tables (>= 0) */
+    int32_t W_cap;    /* BeamKV slots per step: step s, beam k -> s * W_cap + k */
+    int32_t reserved; /* must be 0 */
+    int64_t beam_cap; /* BeamKV tokens per request in beam_k / beam_v (>= 0) */
+} gr_beam_step_dims;
+
+/*
+ * One decode step of the per-beam state: BeamKV append and BeamPath update.
+ * BeamKV keeps each beam's short decode history.  BeamPath records how beams
+ * fork and reorder by index, so that beam selection never copies KV (GR-Inference
+ * blog, section on system design; SID-GR README, "Design Highlights": BeamPath
+ * keeps the parent-child relation).  The history is reached token by token through
+ * direct indices (xGR review, section "xAttention", KV cache management).
+ *
+ * Request b had W_old = row_offset_old[b+1] - row_offset_old[b] beams with
+ * paths of s = beam_len_old[b] tokens.  Beam selection left it W_new =
+ * row_offset_new[b+1] - row_offset_new[b] beams.  New beam k (packed row
+ * r = row_offset_new[b] + k) descends from old beam parent[r] of request b
+ * (read only when s > 0), and its current token is step s:
+ *   path_new[r][t]              = path_old[row_offset_old[b] + parent[r]][t]   t < s
+ *   path_new[r][s]              = s * W_cap + k
+ *   beam_k[b][s * W_cap + k][:] = new_k[r][:]      (all KV heads; beam_v likewise)
+ *   beam_len_new[b]             = W_new > 0 ? s + 1 : s
+ * Nothing else is written: entries t > s of path_new and every other BeamKV
+ * slot keep their contents.  The paths go to a second table, so no row is
+ * overwritten before another reads it.
+ *
+ * Layouts (row-major, contiguous; DEVICE memory except dims):
+ *   row_offset_old, row_offset_new  int32 [B+1]
+ *   parent                          int32 [R_new]
+ *   path_old                        int32 [R_old][T_cap]
+ *   path_new                        int32 [R_new][T_cap]
+ *   beam_len_old, beam_len_new      int32 [B]
+ *   new_k, new_v                    bf16  [R_new][Hkv][D]
+ *   beam_k, beam_v                  bf16  [B][beam_cap][Hkv][D], updated in place
+ *   violations                      int32 [1] or NULL
+ *
+ * A row whose step or slot is out of range (s >= T_cap, k >= W_cap,
+ * s * W_cap + k >= beam_cap), or with s > 0 and parent[r] outside
+ * [0, W_old), writes nothing.  When violations is not NULL, the number of
+ * such rows is added to *violations (the caller zeroes it).
+ *
+ * path_new must not overlap path_old, and beam_len_new must not overlap
+ * beam_len_old (both are checked: GR_ERR_DIMS).  new_k / new_v must not overlap
+ * beam_k / beam_v.  Ownership, threading, graph capture and the other error codes
+ * are as for gr_decode_attn.  Writes are bit copies, so results are exact.
+ */
+int gr_beam_step(const gr_beam_step_dims *dims, const int32_t *row_offset_old,
+                 const int32_t *row_offset_new, const int32_t *parent,
+                 const int32_t *path_old, const int32_t *beam_len_old, const void *new_k,
+                 const void *new_v, int32_t *path_new, int32_t *beam_len_new, void *beam_k,
+                 void *beam_v, int32_t *violations, void *stream);
+
 /* Static description of a status code. */
 const char *gr_status_str(int status);
 

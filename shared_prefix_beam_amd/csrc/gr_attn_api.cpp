@@ -252,6 +252,75 @@ int gr_check_metadata(const gr_decode_attn_dims *d, const int32_t *row_offset,
     return e == hipSuccess ? GR_OK : GR_ERR_LAUNCH;
 }
 
+int gr_beam_step(const gr_beam_step_dims *d, const int32_t *row_offset_old,
+                 const int32_t *row_offset_new, const int32_t *parent, const int32_t *path_old,
+                 const int32_t *beam_len_old, const void *new_k, const void *new_v,
+                 int32_t *path_new, int32_t *beam_len_new, void *beam_k, void *beam_v,
+                 int32_t *violations, void *stream)
+{
+    if (!d)
+        return GR_ERR_NULL;
+    if (d->B < 0 || d->R_old < 0 || d->R_new < 0 || d->Hkv <= 0 || d->T_cap < 0 ||
+        d->W_cap < 0 || d->beam_cap < 0 || d->reserved != 0)
+        return GR_ERR_DIMS;
+    if (d->D != 64 && d->D != 128)
+        return GR_ERR_UNSUPPORTED;
+    if (d->B > 0 && (!row_offset_old || !row_offset_new || !beam_len_old || !beam_len_new))
+        return GR_ERR_NULL;
+    if (d->R_new > 0 && (!parent || !new_k || !new_v || !beam_k || !beam_v ||
+                         (d->T_cap > 0 && !path_new)))
+        return GR_ERR_NULL;
+    if (d->R_old > 0 && d->T_cap > 0 && !path_old)
+        return GR_ERR_NULL;
+    const void *bf[] = {new_k, new_v, beam_k, beam_v};
+    for (const void *p : bf)
+        if (p && !aligned16(p))
+            return GR_ERR_ALIGN;
+    const void *i32[] = {row_offset_old, row_offset_new, parent, path_old, beam_len_old,
+                         path_new, beam_len_new, violations};
+    for (const void *p : i32)
+        if (p && (reinterpret_cast<uintptr_t>(p) & 3u))
+            return GR_ERR_ALIGN;
+    // the step reads path_old / beam_len_old while it writes path_new /
+    // beam_len_new: the ranges must be disjoint
+    auto overlap = [](const void *a, int64_t na, const void *b, int64_t nb) {
+        const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+        return a && b && na > 0 && nb > 0 && x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+    };
+    if (overlap(path_old, (int64_t)d->R_old * d->T_cap * 4, path_new,
+                (int64_t)d->R_new * d->T_cap * 4) ||
+        overlap(beam_len_old, (int64_t)d->B * 4, beam_len_new, (int64_t)d->B * 4))
+        return GR_ERR_DIMS;
+    if (d->B == 0)
+        return GR_OK;
+    int st = device_ok();
+    if (st != GR_OK)
+        return st;
+    gr::StepParams p{};
+    p.row_offset_old = row_offset_old;
+    p.row_offset_new = row_offset_new;
+    p.parent = parent;
+    p.path_old = path_old;
+    p.len_old = beam_len_old;
+    p.new_k = static_cast<const uint16_t *>(new_k);
+    p.new_v = static_cast<const uint16_t *>(new_v);
+    p.path_new = path_new;
+    p.len_new = beam_len_new;
+    p.beam_k = static_cast<uint16_t *>(beam_k);
+    p.beam_v = static_cast<uint16_t *>(beam_v);
+    p.violations = violations;
+    p.B = d->B;
+    p.R_old = d->R_old;
+    p.R_new = d->R_new;
+    p.Hkv = d->Hkv;
+    p.D = d->D;
+    p.T_cap = d->T_cap;
+    p.W_cap = d->W_cap;
+    p.beam_cap = d->beam_cap;
+    const hipError_t e = gr::launch_beam_step(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GR_OK : GR_ERR_LAUNCH;
+}
+
 const char *gr_status_str(int status)
 {
     switch (status) {

@@ -24,6 +24,17 @@ struct MetaCheck {
     int64_t ctx_cap, beam_cap;
 };
 
+// One beam step (BeamKV append + BeamPath update).
+struct StepParams {
+    const int32_t *row_offset_old, *row_offset_new, *parent, *path_old, *len_old;
+    const uint16_t *new_k, *new_v;
+    int32_t *path_new, *len_new;
+    uint16_t *beam_k, *beam_v;
+    int32_t *violations;   // may be null
+    int B, R_old, R_new, Hkv, D, T_cap, W_cap;
+    int64_t beam_cap;
+};
+
 // Longest key list the generic comparator keeps in LDS.
 constexpr int GENERIC_MAX_KEYS = 16320;
 
@@ -38,5 +49,6 @@ int fused_lds_bytes(int D, int nqt, int nks);
 hipError_t launch_fused(const Params &p, int nqt, int nks, int grid, hipStream_t s);
 hipError_t launch_generic(const Params &p, hipStream_t s);
 hipError_t launch_check(const MetaCheck &c, hipStream_t s);
+hipError_t launch_beam_step(const StepParams &p, hipStream_t s);
 
 }  // namespace gr

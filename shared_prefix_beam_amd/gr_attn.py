@@ -5,8 +5,8 @@ current HIP stream; every step of the computation runs in libgr_attn.so.
 Loading fails loudly when the library has not been built.
 
 Functions with the C names take the same arguments as the C entry points
-(a ``Dims`` struct plus raw pointers); ``decode_attn`` / ``decode_attn_generic``
-/ ``check_metadata`` accept torch tensors.
+(a dims struct plus raw pointers); ``decode_attn`` / ``decode_attn_generic``
+/ ``check_metadata`` / ``beam_step`` accept torch tensors.
 """
 from __future__ import annotations
 
@@ -26,7 +26,7 @@ GR_ERR_LAUNCH = -5
 GR_ERR_DEVICE = -6
 
 EXPORTS = ("gr_decode_attn", "gr_decode_attn_generic", "gr_check_metadata",
-           "gr_status_str", "gr_version")
+           "gr_beam_step", "gr_status_str", "gr_version")
 
 
 class Dims(ctypes.Structure):
@@ -37,6 +37,15 @@ class Dims(ctypes.Structure):
                 ("T_cap", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("ctx_cap", ctypes.c_int64), ("beam_cap", ctypes.c_int64),
                 ("scale", ctypes.c_float), ("flags", ctypes.c_int32)]
+
+
+class StepDims(ctypes.Structure):
+    """``gr_beam_step_dims`` (host memory)."""
+
+    _fields_ = [("B", ctypes.c_int32), ("R_old", ctypes.c_int32), ("R_new", ctypes.c_int32),
+                ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32), ("T_cap", ctypes.c_int32),
+                ("W_cap", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("beam_cap", ctypes.c_int64)]
 
 
 class GrAttnError(RuntimeError):
@@ -65,6 +74,8 @@ def load() -> ctypes.CDLL:
             fn.restype = ctypes.c_int
         lib.gr_check_metadata.argtypes = [DP, P, P, P, P, P, P]
         lib.gr_check_metadata.restype = ctypes.c_int
+        lib.gr_beam_step.argtypes = [ctypes.POINTER(StepDims)] + [P] * 13
+        lib.gr_beam_step.restype = ctypes.c_int
         lib.gr_status_str.argtypes = [ctypes.c_int]
         lib.gr_status_str.restype = ctypes.c_char_p
         lib.gr_version.argtypes = []
@@ -91,6 +102,14 @@ def gr_check_metadata(dims: Dims, row_offset, ctx_len, beam_path, beam_len, viol
                       stream) -> int:
     return load().gr_check_metadata(ctypes.byref(dims), row_offset, ctx_len, beam_path,
                                     beam_len, violations, stream)
+
+
+def gr_beam_step(dims: StepDims, row_offset_old, row_offset_new, parent, path_old,
+                 beam_len_old, new_k, new_v, path_new, beam_len_new, beam_k, beam_v, violations,
+                 stream) -> int:
+    return load().gr_beam_step(ctypes.byref(dims), row_offset_old, row_offset_new, parent,
+                               path_old, beam_len_old, new_k, new_v, path_new, beam_len_new,
+                               beam_k, beam_v, violations, stream)
 
 
 def gr_status_str(status: int) -> str:
@@ -199,3 +218,47 @@ def check_metadata(ctx_len, beam_path, beam_len, row_offset, *, B, R, Hq, Hkv, D
     if st != GR_OK:
         raise GrAttnError(st, "gr_check_metadata")
     return violations
+
+
+def beam_step(row_offset_old, row_offset_new, parent, path_old, beam_len_old, new_k, new_v,
+              path_new, beam_len_new, beam_k, beam_v, W_cap: int, violations=None,
+              stream=None):
+    """BeamKV append + BeamPath update of one decode step (include/gr_attn.h).
+
+    Writes ``path_new``, ``beam_len_new`` and the new slots of ``beam_k`` /
+    ``beam_v`` in place; enqueued on ``stream`` (default: torch's current
+    one).  ``violations`` (int32 [1] on the device, or None) accumulates the
+    rows skipped as out of range.
+    """
+    import torch
+    for name, t, dt in (("row_offset_old", row_offset_old, torch.int32),
+                        ("row_offset_new", row_offset_new, torch.int32),
+                        ("parent", parent, torch.int32), ("path_old", path_old, torch.int32),
+                        ("beam_len_old", beam_len_old, torch.int32),
+                        ("new_k", new_k, torch.bfloat16), ("new_v", new_v, torch.bfloat16),
+                        ("path_new", path_new, torch.int32),
+                        ("beam_len_new", beam_len_new, torch.int32),
+                        ("beam_k", beam_k, torch.bfloat16), ("beam_v", beam_v, torch.bfloat16)):
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    B, beam_cap, Hkv, D = beam_k.shape
+    if beam_v.shape != beam_k.shape or new_v.shape != new_k.shape:
+        raise ValueError("K and V shapes differ")
+    R_new = new_k.shape[0]
+    if new_k.shape[1:] != (Hkv, D) or path_new.shape[0] != R_new or parent.numel() < R_new:
+        raise ValueError("new-row shapes mismatch")
+    if row_offset_old.numel() != B + 1 or row_offset_new.numel() != B + 1 \
+            or beam_len_old.numel() != B or beam_len_new.numel() != B:
+        raise ValueError("request count mismatch")
+    if path_old.dim() != 2 or path_old.shape[1] != path_new.shape[1]:
+        raise ValueError("BeamPath tables must share T_cap")
+    dims = StepDims(B=B, R_old=path_old.shape[0], R_new=R_new, Hkv=Hkv, D=D,
+                    T_cap=path_new.shape[1], W_cap=int(W_cap), reserved=0, beam_cap=beam_cap)
+    st = gr_beam_step(dims, _ptr(row_offset_old), _ptr(row_offset_new), _ptr(parent),
+                      _ptr(path_old), _ptr(beam_len_old), _ptr(new_k), _ptr(new_v),
+                      _ptr(path_new), _ptr(beam_len_new), _ptr(beam_k), _ptr(beam_v),
+                      _ptr(violations), _stream_handle(stream))
+    if st != GR_OK:
+        raise GrAttnError(st, "gr_beam_step")

@@ -74,9 +74,9 @@ def grow(fn: StepFn, B: int, Hkv: int, D: int, widths: List[List[int]], T_cap: i
 WIDTHS = [[3, 3, 3, 3, 3], [1, 2, 4, 5, 6], [4, 4, 0, 0, 0], [5, 4, 3, 2, 2]]
 
 
-def pin_p1_chain_walk(fn: StepFn, seed: int = 3):
+def pin_p1_chain_walk(fn: StepFn, seed: int = 3, Hkv: int = 2, D: int = 8):
     B, T_cap, W_cap = len(WIDTHS), 6, 6
-    steps = grow(fn, B, 2, 8, WIDTHS, T_cap, W_cap, seed)
+    steps = grow(fn, B, Hkv, D, WIDTHS, T_cap, W_cap, seed)
     for st in steps:
         s = st["s"]
         assert st["skipped"] == 0
@@ -97,9 +97,9 @@ def pin_p1_chain_walk(fn: StepFn, seed: int = 3):
                 assert np.array_equal(st["path_new"][r, s + 1:], st["path_init"][r, s + 1:])
 
 
-def pin_p2_append(fn: StepFn, seed: int = 4):
+def pin_p2_append(fn: StepFn, seed: int = 4, Hkv: int = 3, D: int = 16):
     B, T_cap, W_cap = len(WIDTHS), 6, 6
-    steps = grow(fn, B, 3, 16, WIDTHS, T_cap, W_cap, seed)
+    steps = grow(fn, B, Hkv, D, WIDTHS, T_cap, W_cap, seed)
     for st in steps:
         s = st["s"]
         written = np.zeros(st["bk"].shape[:2], dtype=bool)
@@ -171,9 +171,9 @@ def pin_p3_composition(fn: StepFn, seed: int = 5):
                 assert np.max(np.abs(out[r, h] - ref)) < 1e-12, (b, k, h)
 
 
-def pin_p4_special(fn: StepFn):
+def pin_p4_special(fn: StepFn, Hkv: int = 1, D: int = 4):
     rng = np.random.default_rng(9)
-    B, Hkv, D, T_cap, W_cap = 3, 1, 4, 3, 4
+    B, T_cap, W_cap = 3, 3, 4
     beam_cap = T_cap * W_cap + 1
     bk = rng.integers(0, 1 << 16, size=(B, beam_cap, Hkv, D), dtype=np.uint16)
     bv = bk.copy()

@@ -96,3 +96,66 @@ def test_generic_rejects_too_long_context():
     d = good_dims(ctx_cap=20000)
     st = gr_attn.gr_decode_attn_generic(d, *([P16] * 11), None)
     assert st == gr_attn.GR_ERR_UNSUPPORTED
+
+
+# ---- gr_beam_step host validation ------------------------------------------
+def test_step_dims_struct_layout():
+    # int32 x8, int64 -> 40 bytes, beam_cap at 32
+    assert ctypes.sizeof(gr_attn.StepDims) == 40
+    assert gr_attn.StepDims.beam_cap.offset == 32
+
+
+def step_dims(**over):
+    d = dict(B=2, R_old=6, R_new=8, Hkv=8, D=128, T_cap=4, W_cap=4, reserved=0, beam_cap=17)
+    d.update(over)
+    return gr_attn.StepDims(**d)
+
+
+def step_call(dims, **ptrs):
+    # path_old and path_new in separate fake ranges (R * T_cap * 4 bytes apart)
+    args = dict(ro_old=P16, ro_new=P16, parent=P16, path_old=P16, len_old=P16, new_k=P16,
+                new_v=P16, path_new=P16 * 2, len_new=P16 * 3, beam_k=P16, beam_v=P16,
+                violations=None)
+    args.update(ptrs)
+    return gr_attn.gr_beam_step(dims, args["ro_old"], args["ro_new"], args["parent"],
+                                args["path_old"], args["len_old"], args["new_k"], args["new_v"],
+                                args["path_new"], args["len_new"], args["beam_k"],
+                                args["beam_v"], args["violations"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(B=-1), gr_attn.GR_ERR_DIMS),
+    (dict(R_new=-1), gr_attn.GR_ERR_DIMS),
+    (dict(Hkv=0), gr_attn.GR_ERR_DIMS),
+    (dict(W_cap=-1), gr_attn.GR_ERR_DIMS),
+    (dict(beam_cap=-1), gr_attn.GR_ERR_DIMS),
+    (dict(reserved=3), gr_attn.GR_ERR_DIMS),
+    (dict(D=96), gr_attn.GR_ERR_UNSUPPORTED),
+])
+def test_step_bad_dims_rejected(over, code):
+    assert step_call(step_dims(**over)) == code
+
+
+@pytest.mark.parametrize("which", ["ro_old", "ro_new", "parent", "new_k", "new_v", "path_new",
+                                   "len_old", "len_new", "beam_k", "beam_v", "path_old"])
+def test_step_null_pointer_rejected(which):
+    assert step_call(step_dims(), **{which: None}) == gr_attn.GR_ERR_NULL
+
+
+def test_step_null_dims_rejected():
+    assert gr_attn.load().gr_beam_step(None, *([None] * 13)) == gr_attn.GR_ERR_NULL
+
+
+@pytest.mark.parametrize("which", ["new_k", "beam_v"])
+def test_step_misaligned_bf16_rejected(which):
+    assert step_call(step_dims(), **{which: P16 + 8}) == gr_attn.GR_ERR_ALIGN
+
+
+def test_step_overlapping_tables_rejected():
+    # path_new starting inside path_old's R_old * T_cap * 4 bytes
+    assert step_call(step_dims(), path_new=P16 + 16) == gr_attn.GR_ERR_DIMS
+    assert step_call(step_dims(), len_new=P16 + 4, len_old=P16) == gr_attn.GR_ERR_DIMS
+
+
+def test_step_empty_batch_is_a_no_op():
+    assert step_call(step_dims(B=0, R_old=0, R_new=0)) == gr_attn.GR_OK
