@@ -10,7 +10,10 @@ Infinity Cache) that every step reads them from HBM.
 
 Prints ONE JSON line.  The headline workload is the Qwen3-0.6B attention
 shape at 128 beams (B=8, ctx 1024, HBM-bound); the 900-beam workload
-(MFMA-bound) is measured the same way and reported under "secondary".
+(MFMA-bound) is measured the same way and reported under "secondary".  The
+per-beam state update of the same decode step (gr_beam_step: BeamKV append
++ BeamPath update, HBM-bound) is reported under "beam_step" at the 900- and
+128-beam shapes.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
 """
@@ -38,6 +41,8 @@ PRIMARY = 2                   # Qwen3-0.6B shape, W=128
 SECONDARY = 4                 # Qwen3-0.6B shape, W=900
 KERNEL_SOURCES = ["shared_prefix_beam_amd/csrc/gr_attn_kernels.hip",
                   "shared_prefix_beam_amd/csrc/gr_attn_api.cpp"]
+STEP_SOURCES = ["shared_prefix_beam_amd/csrc/gr_beam_step.hip"]
+STEP_CFGS = (4, 2)            # beam-step shapes reported (900 and 128 beams)
 
 
 def algorithmic(inp: I.Inputs):
@@ -62,21 +67,36 @@ def algorithmic(inp: I.Inputs):
     return nbytes, flops
 
 
-def kernel_hash() -> str:
+def algorithmic_step(st: I.StepInputs) -> int:
+    """Bytes one beam step must move, each once: the new K and V rows read
+    and written into their slots, the parent index, the parent's s path
+    entries read and s+1 entries written, and per request the two lengths
+    and two row offsets."""
+    s = st.state
+    row = s.wl.Hkv * s.wl.D * 2                        # bytes of one token's K (or V)
+    nbytes = 0
+    for b in range(s.B):
+        w_new = int(st.row_offset_new[b + 1] - st.row_offset_new[b])
+        t = int(s.beam_len[b])
+        nbytes += w_new * (4 * row + 4 + 4 * t + 4 * (t + 1)) + 16
+    return nbytes
+
+
+def kernel_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in (KERNEL_SOURCES if sources is None else sources):
         h.update(open(os.path.join(ROOT, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str):
+def recorded_traffic(workload: str, kernel: str = "fused_decode_attn", sources=None):
     """HBM traffic per launch from a committed rocprofv3 --pmc summary, if it
     was taken from the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", f"traffic_fused_decode_attn_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_sha") != kernel_hash():
+    if rec.get("kernel_sha") != kernel_hash(sources):
         return None
     return rec.get("bytes_per_launch")
 
@@ -181,6 +201,53 @@ def write_profile_summaries(d: str):
                    "fetch_factor": f_fetch, "write_factor": f_write, "avg_launch_us": avg_us},
                   open(os.path.join(out_dir, f"traffic_{name}.json"), "w"), indent=1)
         print(f"wrote profiles/{name}.txt", flush=True)
+    write_step_profile(d, f_fetch, f_write, copy_fetch_kib, copy_write_kib)
+
+
+def write_step_profile(d, f_fetch, f_write, copy_fetch_kib, copy_write_kib):
+    """The same summary for the beam-step kernel (profiled with --only beam_step)."""
+    if not os.path.isdir(os.path.join(d, "trace_beam_step")):
+        return
+    st = I.step_workload(STEP_CFGS[0])
+    name_wl = I.STEP_WORKLOADS[STEP_CFGS[0]]["name"]
+    nbytes = algorithmic_step(st)
+    stats = _csv_rows(os.path.join(d, "trace_beam_step"), "kernel_stats.csv")
+    fetch_kib, n_f = _counter_per_dispatch(os.path.join(d, "fetch_beam_step"), "beam_step",
+                                          "FETCH_SIZE")
+    write_kib, n_w = _counter_per_dispatch(os.path.join(d, "write_beam_step"), "beam_step",
+                                          "WRITE_SIZE")
+    traffic = fetch_kib * 1024 * f_fetch + write_kib * 1024 * f_write
+    kern = [r for r in stats if "beam_step" in r["Name"]]
+    avg_us = float(kern[0]["AverageNs"]) / 1e3 if kern else float("nan")
+    sha = kernel_hash(STEP_SOURCES)
+    lines = [f"# beam_step on {name_wl}", "",
+             "kernel trace (rocprofv3 --kernel-trace --stats), command from the repository root:",
+             "    " + PROFILE_COMMANDS["trace"].format(d="gpurun_out/prof", w="beam_step"), "",
+             f"{'kernel':60s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
+    for r in stats:
+        lines.append(f"{r['Name'][:60]:60s} {int(r['Calls']):6d} "
+                     f"{float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
+                     f"{float(r['MaxNs']) / 1e3:9.2f}")
+    lines += ["", "HBM counters, one pass each:",
+              "    " + PROFILE_COMMANDS["fetch"].format(d="gpurun_out/prof", w="beam_step"),
+              "    " + PROFILE_COMMANDS["write"].format(d="gpurun_out/prof", w="beam_step"),
+              "    (copy calibration as in the attention summaries)", "",
+              f"FETCH_SIZE per dispatch   {fetch_kib:12.1f} KiB  (mean of {n_f})",
+              f"WRITE_SIZE per dispatch   {write_kib:12.1f} KiB  (mean of {n_w})",
+              f"copy factors              fetch {f_fetch:.3f}, write {f_write:.3f}",
+              f"HBM traffic per launch    {traffic / 1e6:12.3f} MB",
+              f"algorithmic bytes         {nbytes / 1e6:12.3f} MB  "
+              f"(traffic / algorithmic = {traffic / nbytes:.3f})",
+              f"average launch            {avg_us:12.2f} us -> {nbytes / avg_us / 1e3:.1f} GB/s",
+              f"kernel sources sha256[:16] {sha}"]
+    name = f"beam_step_{name_wl}"
+    out_dir = os.path.join(ROOT, "profiles")
+    open(os.path.join(out_dir, name + ".txt"), "w").write("\n".join(lines) + "\n")
+    json.dump({"kernel": "beam_step", "workload": name_wl, "kernel_sha": sha,
+               "bytes_per_launch": traffic, "fetch_kib": fetch_kib, "write_kib": write_kib,
+               "fetch_factor": f_fetch, "write_factor": f_write, "avg_launch_us": avg_us},
+              open(os.path.join(out_dir, f"traffic_{name}.json"), "w"), indent=1)
+    print(f"wrote profiles/{name}.txt", flush=True)
 
 
 def measure(cfg: int, steps: int, warmup: int):
@@ -252,6 +319,82 @@ def measure(cfg: int, steps: int, warmup: int):
                 launch_ms=launch_ms, n_sets=n_sets, spot_abs=spot, spot_lse=spot_lse)
 
 
+def measure_step(cfg: int, steps: int, warmup: int):
+    """Time gr_beam_step on the step workload `cfg` the way `measure` times
+    the attention: rotating input sets, direct C calls, one event pair."""
+    import torch
+    from shared_prefix_beam_amd import gr_attn
+
+    st = I.step_workload(cfg)
+    s = st.state
+    nbytes = algorithmic_step(st)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+    base = dict(ro_old=i32(s.row_offset), ro_new=i32(st.row_offset_new), parent=i32(st.parent),
+                path_old=i32(s.beam_path), len_old=i32(s.beam_len), new_k=bf(st.new_k),
+                new_v=bf(st.new_v), path_new=i32(np.zeros((st.R_new, s.T_cap), np.int32)),
+                len_new=i32(np.zeros(s.B, np.int32)), beam_k=bf(s.beam_k), beam_v=bf(s.beam_v))
+    n_sets = max(2, int(np.ceil(2 * MALL_BYTES / nbytes)) + 1)
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(n_sets - 1)]
+    stream = torch.cuda.current_stream()
+    for t in sets:   # the front end validates every set once
+        gr_attn.beam_step(t["ro_old"], t["ro_new"], t["parent"], t["path_old"], t["len_old"],
+                          t["new_k"], t["new_v"], t["path_new"], t["len_new"], t["beam_k"],
+                          t["beam_v"], s.W_cap, stream=stream)
+    dims = gr_attn.StepDims(B=s.B, R_old=s.R, R_new=st.R_new, Hkv=s.wl.Hkv, D=s.wl.D,
+                            T_cap=s.T_cap, W_cap=s.W_cap, reserved=0, beam_cap=s.beam_cap)
+    order = ("ro_old", "ro_new", "parent", "path_old", "len_old", "new_k", "new_v", "path_new",
+             "len_new", "beam_k", "beam_v")
+    args = [tuple(t[k].data_ptr() for k in order) + (None,) for t in sets]
+    handle = stream.cuda_stream
+
+    def step(i):
+        rc = gr_attn.gr_beam_step(dims, *args[i % n_sets], handle)
+        if rc != gr_attn.GR_OK:
+            raise gr_attn.GrAttnError(rc, "gr_beam_step")
+
+    for i in range(warmup):
+        step(i)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    launch_ms = ev0.elapsed_time(ev1) / steps
+    # bit-exact spot check of the first set against the oracle (not timed)
+    from oracle import oracle as O
+    ref_path, ref_len, ref_k, ref_v, _ = O.beam_step(
+        s.row_offset, st.row_offset_new, st.parent, s.beam_path, s.beam_len, st.new_k,
+        st.new_v, np.zeros((st.R_new, s.T_cap), np.int32), s.beam_k, s.beam_v, s.W_cap)
+    ok = (np.array_equal(base["path_new"].cpu().numpy(), ref_path)
+          and np.array_equal(base["len_new"].cpu().numpy(), ref_len)
+          and np.array_equal(base["beam_k"].view(torch.int16).cpu().numpy().view(np.uint16),
+                             ref_k)
+          and np.array_equal(base["beam_v"].view(torch.int16).cpu().numpy().view(np.uint16),
+                             ref_v))
+    return dict(st=st, name=I.STEP_WORKLOADS[cfg]["name"], nbytes=nbytes, launch_ms=launch_ms,
+                n_sets=n_sets, bit_exact=bool(ok))
+
+
+def step_entry(r) -> dict:
+    gbs = r["nbytes"] / (r["launch_ms"] * 1e-3) / 1e9
+    return {"workload": r["name"], "rows": r["st"].R_new, "launch_us": r["launch_ms"] * 1e3,
+            "value": r["st"].R_new / (r["launch_ms"] * 1e-3), "unit": "beam-rows/s",
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS,
+                         "traffic": recorded_traffic(r["name"], "beam_step", STEP_SOURCES),
+                         "kernel": "beam_step", "algorithmic_bytes": r["nbytes"]},
+            "input_copies_rotated": r["n_sets"], "bit_exact": r["bit_exact"]}
+
+
 def cpu_baseline(inp: I.Inputs, min_seconds: float = 10.0):
     """The fp64 oracle on the host cores: repeated passes over every row of
     the workload until about `min_seconds` of wall time have been spent."""
@@ -278,7 +421,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--only", choices=["primary", "secondary"],
+    ap.add_argument("--only", choices=["primary", "secondary", "beam_step"],
                     help="time one workload only and print its launch time (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run 10 device copies of 256 MiB (reference for HBM byte counters)")
@@ -306,6 +449,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": 256 << 20, "launches": 10}), flush=True)
+        return
+    if args.only == "beam_step":
+        r = measure_step(STEP_CFGS[0], args.steps, args.warmup)
+        print(json.dumps({"workload": r["name"], "launch_us": r["launch_ms"] * 1e3,
+                          "bit_exact": r["bit_exact"]}), flush=True)
         return
     if args.only:
         r = measure(PRIMARY if args.only == "primary" else SECONDARY, args.steps, args.warmup)
@@ -354,6 +502,7 @@ def main():
                          "hbm_GBps": sec["nbytes"] / (sec["launch_ms"] * 1e-3) / 1e9},
             "spot_check": {"max_abs": sec["spot_abs"], "lse_abs": sec["spot_lse"]},
         }
+    line["beam_step"] = [step_entry(measure_step(c, args.steps, args.warmup)) for c in STEP_CFGS]
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line), flush=True)
