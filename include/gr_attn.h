@@ -109,6 +109,35 @@ int gr_decode_attn_generic(const gr_decode_attn_dims *dims, const int32_t *row_o
                            const int32_t *beam_path, const int32_t *beam_len, void *out,
                            float *lse, void *stream);
 
+/* Paged ContextKV: fixed-size pages of a shared pool.  Host memory; read
+ * only during the call (the pointers are DEVICE pointers). */
+typedef struct gr_paged_ctx {
+    const void *k_pages;       /* bf16 [n_pages][page_size][Hkv][D] */
+    const void *v_pages;       /* bf16 [n_pages][page_size][Hkv][D] */
+    const int32_t *page_table; /* int32 [B][pages_per_req]: page of each request's
+                                  logical page j (tokens j*page_size ..) */
+    int32_t page_size;         /* tokens per page: a positive multiple of 16 */
+    int32_t pages_per_req;     /* row stride of page_table */
+    int64_t n_pages;           /* pages in each pool (>= 1) */
+} gr_paged_ctx;
+
+/*
+ * gr_decode_attn with the ContextKV read through a page table instead of a
+ * dense per-request slice.  Page tables in decode attention are on the SID-GR
+ * roadmap (SID-GR README, "Roadmap").  Token j < ctx_len[b] of request b is
+ * row j % page_size of page page_table[b][j / page_size]; within a page the
+ * rows have the dense layout ([Hkv][D] per token).  Every other argument,
+ * the result, the ownership and the errors are those of gr_decode_attn;
+ * dims->ctx_cap must not exceed pages_per_req * page_size and bounds
+ * ctx_len.  Entries of page_table for tokens < ctx_len[b] must lie in
+ * [0, n_pages) (an entry outside is clamped into the pool: wrong data, no
+ * access outside the buffers).
+ */
+int gr_decode_attn_paged(const gr_decode_attn_dims *dims, const gr_paged_ctx *ctx,
+                         const int32_t *row_offset, const void *q, const int32_t *ctx_len,
+                         const void *beam_k, const void *beam_v, const int32_t *beam_path,
+                         const int32_t *beam_len, void *out, float *lse, void *stream);
+
 /*
  * Device-side check of the metadata preconditions above: row_offset is
  * non-decreasing with row_offset[0] = 0, row_offset[B] = R and every

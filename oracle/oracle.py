@@ -183,3 +183,33 @@ def beam_step_from_library(path: str):
     def fn(*args, **kw):
         return beam_step(*args, lib=lib, **kw)
     return fn
+
+
+def gather_pages(k_pages, v_pages, page_table, page_size: int, ctx_len, ctx_cap: int):
+    """Dense ContextKV [B][ctx_cap][Hkv][D] from pages: token j < ctx_len[b] of
+    request b is row j % page_size of page page_table[b][j // page_size]
+    (tokens past ctx_len are NaN).  A plain loop over tokens; the page
+    layout is the only thing it adds to the dense definition."""
+    page_table = np.asarray(page_table)
+    B = page_table.shape[0]
+    _, ps, Hkv, D = k_pages.shape
+    assert ps == page_size
+    k = np.full((B, ctx_cap, Hkv, D), 0x7FC0, dtype=np.uint16)
+    v = np.full((B, ctx_cap, Hkv, D), 0x7FC0, dtype=np.uint16)
+    for b in range(B):
+        for j in range(int(ctx_len[b])):
+            page = int(page_table[b, j // page_size])
+            k[b, j] = k_pages[page, j % page_size]
+            v[b, j] = v_pages[page, j % page_size]
+    return k, v
+
+
+def decode_attn_paged(q, k_pages, v_pages, page_table, page_size, ctx_len, beam_k, beam_v,
+                      beam_path, beam_len, row_offset, ctx_cap=None, scale=None, rows=None,
+                      n_threads=None):
+    """``decode_attn`` over a paged ContextKV (gathered to dense first)."""
+    if ctx_cap is None:
+        ctx_cap = max(int(np.max(ctx_len, initial=0)), 1)
+    k, v = gather_pages(k_pages, v_pages, page_table, page_size, ctx_len, ctx_cap)
+    return decode_attn(q, k, v, ctx_len, beam_k, beam_v, beam_path, beam_len, row_offset,
+                       scale=scale, rows=rows, n_threads=n_threads)

@@ -197,6 +197,49 @@ int gr_decode_attn(const gr_decode_attn_dims *d, const int32_t *row_offset, cons
     return e == hipSuccess ? GR_OK : GR_ERR_LAUNCH;
 }
 
+int gr_decode_attn_paged(const gr_decode_attn_dims *d, const gr_paged_ctx *c,
+                         const int32_t *row_offset, const void *q, const int32_t *ctx_len,
+                         const void *beam_k, const void *beam_v, const int32_t *beam_path,
+                         const int32_t *beam_len, void *out, float *lse, void *stream)
+{
+    int st = validate(d);
+    if (st != GR_OK)
+        return st;
+    if (!c)
+        return GR_ERR_NULL;
+    if (c->page_size <= 0 || c->page_size % 16 != 0 || c->pages_per_req <= 0 ||
+        c->n_pages <= 0 || c->n_pages > INT32_MAX ||
+        d->ctx_cap > static_cast<int64_t>(c->pages_per_req) * c->page_size)
+        return GR_ERR_DIMS;
+    if (d->B > 0 && (!c->k_pages || !c->v_pages || !c->page_table))
+        return GR_ERR_NULL;
+    if ((c->k_pages && !aligned16(c->k_pages)) || (c->v_pages && !aligned16(c->v_pages)) ||
+        (reinterpret_cast<uintptr_t>(c->page_table) & 3u))
+        return GR_ERR_ALIGN;
+    st = validate_buffers(d, row_offset, q, c->k_pages, c->v_pages, ctx_len, beam_k, beam_v,
+                          beam_path, beam_len, out, lse);
+    if (st != GR_OK)
+        return st;
+    if (d->R == 0 || d->B == 0 || d->W_max == 0)
+        return GR_OK;
+    st = device_ok();
+    if (st != GR_OK)
+        return st;
+    gr::Params p = make_params(d, row_offset, q, c->k_pages, c->v_pages, ctx_len, beam_k, beam_v,
+                               beam_path, beam_len, out, lse);
+    p.page_table = c->page_table;
+    p.page_size = c->page_size;
+    p.pages_per_req = c->pages_per_req;
+    p.n_pages = c->n_pages;
+    const Plan pl = plan(d);
+    p.n_qt = pl.n_qt;
+    if (pl.grid <= 0)
+        return GR_OK;
+    const hipError_t e =
+        gr::launch_fused(p, pl.nqt, pl.nks, pl.grid, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GR_OK : GR_ERR_LAUNCH;
+}
+
 int gr_decode_attn_generic(const gr_decode_attn_dims *d, const int32_t *row_offset,
                            const void *q, const void *ctx_k, const void *ctx_v,
                            const int32_t *ctx_len, const void *beam_k, const void *beam_v,

@@ -15,6 +15,12 @@ struct Params {
     int64_t ctx_cap, beam_cap;
     float scale_log2;   // softmax scale * log2(e)
     int n_qt;           // query tiles per (request, KV head) pair in the fused grid
+    // Paged ContextKV (fused kernel only): when page_table is set, ctx_k /
+    // ctx_v are page pools [n_pages][page_size][Hkv][D] and token j of request
+    // b is row j % page_size of page page_table[b * pages_per_req + j / page_size].
+    const int32_t *page_table;
+    int page_size, pages_per_req;
+    int64_t n_pages;
 };
 
 struct MetaCheck {

@@ -180,7 +180,7 @@ __device__ __forceinline__ i16x4 lds_tr16(const char *p)
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
 }
 
-template <int D, int NQT, int NKS, int NBUF, int OCC>
+template <int D, int NQT, int NKS, int NBUF, int OCC, bool PAGED>
 __global__ __launch_bounds__(64 * NQT * NKS) __attribute__((amdgpu_waves_per_eu(OCC)))
 void fused_decode_attn(const Params p)
 {
@@ -259,9 +259,20 @@ void fused_decode_attn(const Params p)
     const int iters = (n_tiles + NKS - 1) / NKS;  // same for every wave (barrier count)
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
     const uint32_t stream_off = ks * (NBUF * Gm::TILE);        // byte offset of this stream
-    const uint16_t *kv_k = p.ctx_k + ((int64_t)b * p.ctx_cap * p.Hkv + g) * D;
-    const uint16_t *kv_v = p.ctx_v + ((int64_t)b * p.ctx_cap * p.Hkv + g) * D;
+    // dense: request b's slice; paged: the pools (pages are located per load)
+    const uint16_t *kv_k = p.ctx_k + ((PAGED ? 0 : (int64_t)b * p.ctx_cap * p.Hkv) + g) * D;
+    const uint16_t *kv_v = p.ctx_v + ((PAGED ? 0 : (int64_t)b * p.ctx_cap * p.Hkv) + g) * D;
     const int kv_tok = p.Hkv * D;                 // elements between consecutive tokens
+    const int32_t *ptab = PAGED ? p.page_table + (int64_t)b * p.pages_per_req : nullptr;
+    // element offset, within a pool, of token `tok`'s row (KV head 0): the
+    // rows of one page are consecutive, as in the dense layout.  A page index
+    // outside the pool is clamped into it (a broken table reads wrong data,
+    // never outside the buffer).
+    auto page_row = [&](int tok) -> int64_t {
+        int pg = ((const __attribute__((address_space(4))) int32_t *)(uintptr_t)ptab)[tok / p.page_size];
+        pg = pg < 0 ? 0 : (pg >= p.n_pages ? (int)(p.n_pages - 1) : pg);   // stay in the pool
+        return ((int64_t)pg * p.page_size + tok % p.page_size) * kv_tok;
+    };
     constexpr int RPL = 1024 / Gm::ROW;           // rows covered by one 1 KB load
     constexpr int LPW = (Gm::LOADS + NQT - 1) / NQT;   // loads per wave per tile (max)
 
@@ -286,6 +297,46 @@ void fused_decode_attn(const Params p)
     auto issue_tile = [&](int t, int buf) {
         const int key0 = (t_begin + t) * KT;
         const uint32_t dst0 = lds0 + stream_off + buf * Gm::TILE;
+        if constexpr (PAGED) {
+            // A 1 KB load covers RPL consecutive rows, which lie in one page
+            // (the page size is a multiple of 16 >= RPL and key0 is a
+            // multiple of 32): the page is looked up once per load, wave-
+            // uniformly, and the lane offsets are the dense ones.  Rows past
+            // the context end repeat row L-1, each lane finding its page.
+            if (key0 + KT <= L) {
+#pragma unroll
+                for (int i = 0; i < LPW; ++i) {
+                    const int u = qt + i * NQT;
+                    if (EVEN || u < Gm::LOADS) {
+                        const bool is_v = u >= Gm::LOADS / 2;
+                        const int uu = is_v ? u - Gm::LOADS / 2 : u;
+                        const int tok0 = key0 + uu * RPL;
+                        dma16_s((is_v ? kv_v : kv_k) + page_row(tok0) - (int64_t)uu * RPL * kv_tok,
+                                loff[i], dst0 + (is_v ? Gm::KBYTES : 0) + uu * 1024);
+                    }
+                }
+            } else {
+                // the context's last tile: per-lane rows and pages, one load
+                // at a time (rolled, so that no address is held across loads)
+#pragma unroll 1
+                for (int i = 0; i < LPW; ++i) {
+                    const int u = qt + i * NQT;
+                    if (!EVEN && u >= Gm::LOADS)
+                        break;
+                    const bool is_v = u >= Gm::LOADS / 2;
+                    const int uu = is_v ? u - Gm::LOADS / 2 : u;
+                    const int r = uu * RPL + lane / Gm::CH;
+                    const int c = (lane % Gm::CH) ^ (is_v ? vswz<D>(r) : kswz<D>(r));
+                    const int tok = key0 + r < L ? key0 + r : L - 1;
+                    int pg = ptab[tok / p.page_size];
+                    pg = pg < 0 ? 0 : (pg >= p.n_pages ? (int)(p.n_pages - 1) : pg);
+                    const int64_t row = ((int64_t)pg * p.page_size + tok % p.page_size) * kv_tok;
+                    dma16((is_v ? kv_v : kv_k) + row + 8 * c,
+                          dst0 + (is_v ? Gm::KBYTES : 0) + uu * 1024);
+                }
+            }
+            return;
+        }
         if (key0 + KT <= L) {
             // full tile: loop-invariant offsets, no per-lane arithmetic
 #pragma unroll
@@ -986,11 +1037,11 @@ __global__ void check_metadata(const MetaCheck c)
 __global__ void zero_i32(int32_t *p) { *p = 0; }
 
 // ---------------------------------------------------------------------------
-template <int D, int NQT, int NKS, int NBUF, int OCC>
+template <int D, int NQT, int NKS, int NBUF, int OCC, bool PAGED>
 static hipError_t launch_fused_t(const Params &p, int grid, hipStream_t s)
 {
     constexpr int lds = lds_bytes<D, NQT, NKS, NBUF>();
-    auto kern = fused_decode_attn<D, NQT, NKS, NBUF, OCC>;
+    auto kern = fused_decode_attn<D, NQT, NKS, NBUF, OCC, PAGED>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess)
@@ -1013,7 +1064,8 @@ hipError_t launch_fused(const Params &p, int nqt, int nks, int grid, hipStream_t
 {
 #define GR_LAUNCH_CASE(d, a, c, nb, oc)                                               \
     if (p.D == d && nqt == a && nks == c)                                             \
-        return launch_fused_t<d, a, c, nb, oc>(p, grid, s);
+        return p.page_table ? launch_fused_t<d, a, c, nb, oc, true>(p, grid, s)         \
+                            : launch_fused_t<d, a, c, nb, oc, false>(p, grid, s);
     GR_FOR_EACH_FUSED_CONFIG(GR_LAUNCH_CASE)
 #undef GR_LAUNCH_CASE
     return hipErrorInvalidValue;

@@ -25,8 +25,8 @@ GR_ERR_ALIGN = -4
 GR_ERR_LAUNCH = -5
 GR_ERR_DEVICE = -6
 
-EXPORTS = ("gr_decode_attn", "gr_decode_attn_generic", "gr_check_metadata",
-           "gr_beam_step", "gr_status_str", "gr_version")
+EXPORTS = ("gr_decode_attn", "gr_decode_attn_generic", "gr_decode_attn_paged",
+           "gr_check_metadata", "gr_beam_step", "gr_status_str", "gr_version")
 
 
 class Dims(ctypes.Structure):
@@ -46,6 +46,14 @@ class StepDims(ctypes.Structure):
                 ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32), ("T_cap", ctypes.c_int32),
                 ("W_cap", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("beam_cap", ctypes.c_int64)]
+
+
+class PagedCtx(ctypes.Structure):
+    """``gr_paged_ctx`` (host memory holding device pointers)."""
+
+    _fields_ = [("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p),
+                ("page_table", ctypes.c_void_p), ("page_size", ctypes.c_int32),
+                ("pages_per_req", ctypes.c_int32), ("n_pages", ctypes.c_int64)]
 
 
 class GrAttnError(RuntimeError):
@@ -74,6 +82,8 @@ def load() -> ctypes.CDLL:
             fn.restype = ctypes.c_int
         lib.gr_check_metadata.argtypes = [DP, P, P, P, P, P, P]
         lib.gr_check_metadata.restype = ctypes.c_int
+        lib.gr_decode_attn_paged.argtypes = [DP, ctypes.POINTER(PagedCtx)] + [P] * 10
+        lib.gr_decode_attn_paged.restype = ctypes.c_int
         lib.gr_beam_step.argtypes = [ctypes.POINTER(StepDims)] + [P] * 13
         lib.gr_beam_step.restype = ctypes.c_int
         lib.gr_status_str.argtypes = [ctypes.c_int]
@@ -96,6 +106,13 @@ def gr_decode_attn_generic(dims: Dims, row_offset, q, ctx_k, ctx_v, ctx_len, bea
     return load().gr_decode_attn_generic(ctypes.byref(dims), row_offset, q, ctx_k, ctx_v,
                                          ctx_len, beam_k, beam_v, beam_path, beam_len, out,
                                          lse, stream)
+
+
+def gr_decode_attn_paged(dims: Dims, ctx: PagedCtx, row_offset, q, ctx_len, beam_k, beam_v,
+                         beam_path, beam_len, out, lse, stream) -> int:
+    return load().gr_decode_attn_paged(ctypes.byref(dims), ctypes.byref(ctx), row_offset, q,
+                                       ctx_len, beam_k, beam_v, beam_path, beam_len, out, lse,
+                                       stream)
 
 
 def gr_check_metadata(dims: Dims, row_offset, ctx_len, beam_path, beam_len, violations,
@@ -203,6 +220,52 @@ def decode_attn_generic(q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path, bea
     """Same result through the generic per-row comparator kernel."""
     return _run("generic", q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path, beam_len,
                 row_offset, W_max, scale, out, lse, stream)
+
+
+def decode_attn_paged(q, k_pages, v_pages, page_table, page_size: int, ctx_len, beam_k, beam_v,
+                      beam_path, beam_len, row_offset, W_max: int, ctx_cap: Optional[int] = None,
+                      scale: Optional[float] = None, out=None, lse=None, stream=None):
+    """``decode_attn`` with the ContextKV in pages (include/gr_attn.h,
+    gr_decode_attn_paged): k_pages / v_pages bf16 [n_pages][page_size][Hkv][D],
+    page_table int32 [B][pages_per_req].  ``ctx_cap`` defaults to
+    pages_per_req * page_size."""
+    import torch
+    n_pages, ps, Hkv, D = k_pages.shape
+    if ps != page_size or v_pages.shape != k_pages.shape:
+        raise ValueError("page pool shape mismatch")
+    if page_table.dtype != torch.int32 or not page_table.is_cuda or page_table.dim() != 2 \
+            or not page_table.is_contiguous():
+        raise ValueError("page_table must be a contiguous int32 [B][pages_per_req] device tensor")
+    B, ppr = page_table.shape
+    cap = ppr * page_size if ctx_cap is None else int(ctx_cap)
+    for name, t, dt in (("q", q, torch.bfloat16), ("k_pages", k_pages, torch.bfloat16),
+                        ("v_pages", v_pages, torch.bfloat16), ("ctx_len", ctx_len, torch.int32),
+                        ("beam_k", beam_k, torch.bfloat16), ("beam_v", beam_v, torch.bfloat16),
+                        ("beam_path", beam_path, torch.int32), ("beam_len", beam_len, torch.int32),
+                        ("row_offset", row_offset, torch.int32)):
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} device tensor")
+    if beam_k.shape[0] != B or ctx_len.numel() != B or beam_len.numel() != B \
+            or row_offset.numel() != B + 1 or beam_path.shape[0] != q.shape[0] \
+            or beam_k.shape[2:] != (Hkv, D) or q.shape[2] != D:
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    R, Hq, _ = q.shape
+    dims = Dims(B=B, R=R, Hq=Hq, Hkv=Hkv, D=D, W_max=int(W_max), T_cap=beam_path.shape[1],
+                reserved=0, ctx_cap=cap, beam_cap=beam_k.shape[1],
+                scale=0.0 if scale is None else float(scale), flags=0)
+    ctx = PagedCtx(k_pages=k_pages.data_ptr(), v_pages=v_pages.data_ptr(),
+                   page_table=page_table.data_ptr(), page_size=int(page_size), pages_per_req=ppr,
+                   n_pages=n_pages)
+    st = gr_decode_attn_paged(dims, ctx, _ptr(row_offset), _ptr(q), _ptr(ctx_len), _ptr(beam_k),
+                              _ptr(beam_v), _ptr(beam_path), _ptr(beam_len), _ptr(out),
+                              _ptr(lse), _stream_handle(stream))
+    if st != GR_OK:
+        raise GrAttnError(st, "gr_decode_attn_paged")
+    return out, lse
 
 
 def check_metadata(ctx_len, beam_path, beam_len, row_offset, *, B, R, Hq, Hkv, D, W_max,

@@ -278,6 +278,48 @@ def _build(rng: np.random.Generator, wl: Workload, ctx_len: np.ndarray,
 
 
 @dataclasses.dataclass
+class PagedCtx:
+    """A call's ContextKV scattered over fixed-size pages of a shared pool."""
+
+    k_pages: np.ndarray      # [n_pages][page_size][Hkv][D] u16
+    v_pages: np.ndarray
+    page_table: np.ndarray   # [B][pages_per_req] i32
+    page_size: int
+
+
+def to_paged(inp: Inputs, page_size: int, seed: int, spare: int = 3) -> PagedCtx:
+    """Scatter ``inp``'s ContextKV over pages in a seeded random order.
+
+    Request b's logical page j (tokens j*page_size ..) goes to a distinct
+    physical page; ``spare`` extra pages and the rows past ctx_len are bf16
+    NaN, and table entries past a request's last page point at a NaN page,
+    so a kernel that reads a wrong page or row produces NaN."""
+    rng = np.random.default_rng(seed)
+    ppr = max(-(-inp.ctx_cap // page_size), 1)
+    used = [max(-(-int(inp.ctx_len[b]) // page_size), 0) for b in range(inp.B)]
+    n_pages = sum(used) + spare
+    Hkv, D = inp.wl.Hkv, inp.wl.D
+    k_pages = np.full((n_pages, page_size, Hkv, D), BF16_NAN, dtype=np.uint16)
+    v_pages = np.full_like(k_pages, BF16_NAN)
+    perm = rng.permutation(n_pages)
+    table = np.empty((inp.B, ppr), dtype=np.int32)
+    nxt = 0
+    for b in range(inp.B):
+        for j in range(ppr):
+            if j < used[b]:
+                pg = int(perm[nxt])
+                nxt += 1
+                lo = j * page_size
+                hi = min(lo + page_size, int(inp.ctx_len[b]))
+                k_pages[pg, :hi - lo] = inp.ctx_k[b, lo:hi]
+                v_pages[pg, :hi - lo] = inp.ctx_v[b, lo:hi]
+                table[b, j] = pg
+            else:
+                table[b, j] = int(perm[n_pages - 1 - (j % spare)]) if spare else 0
+    return PagedCtx(k_pages=k_pages, v_pages=v_pages, page_table=table, page_size=page_size)
+
+
+@dataclasses.dataclass
 class StepInputs:
     """One BeamKV-append + BeamPath-update call and the state it applies to.
 

@@ -159,3 +159,40 @@ def test_step_overlapping_tables_rejected():
 
 def test_step_empty_batch_is_a_no_op():
     assert step_call(step_dims(B=0, R_old=0, R_new=0)) == gr_attn.GR_OK
+
+
+# ---- gr_decode_attn_paged host validation ----------------------------------
+def paged_call(dims, ctx):
+    return gr_attn.gr_decode_attn_paged(dims, ctx, P16, P16, P16, P16, P16, P16, P16, P16, P16,
+                                        None)
+
+
+def good_ctx(**over):
+    c = dict(k_pages=P16, v_pages=P16, page_table=P16, page_size=16, pages_per_req=4,
+             n_pages=9)
+    c.update(over)
+    return gr_attn.PagedCtx(**c)
+
+
+def test_paged_ctx_struct_layout():
+    assert ctypes.sizeof(gr_attn.PagedCtx) == 40
+    assert gr_attn.PagedCtx.n_pages.offset == 32
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(page_size=24), gr_attn.GR_ERR_DIMS),
+    (dict(page_size=0), gr_attn.GR_ERR_DIMS),
+    (dict(pages_per_req=0), gr_attn.GR_ERR_DIMS),
+    (dict(n_pages=0), gr_attn.GR_ERR_DIMS),
+    (dict(pages_per_req=3), gr_attn.GR_ERR_DIMS),     # ctx_cap 64 > 3 * 16
+    (dict(k_pages=None), gr_attn.GR_ERR_NULL),
+    (dict(page_table=None), gr_attn.GR_ERR_NULL),
+    (dict(v_pages=P16 + 8), gr_attn.GR_ERR_ALIGN),
+])
+def test_paged_bad_ctx_rejected(over, code):
+    assert paged_call(good_dims(), good_ctx(**over)) == code
+
+
+def test_paged_null_ctx_rejected():
+    assert gr_attn.load().gr_decode_attn_paged(ctypes.byref(good_dims()), None,
+                                               *([None] * 10)) == gr_attn.GR_ERR_NULL
