@@ -43,6 +43,7 @@ KERNEL_SOURCES = ["shared_prefix_beam_amd/csrc/gr_attn_kernels.hip",
                   "shared_prefix_beam_amd/csrc/gr_attn_api.cpp"]
 STEP_SOURCES = ["shared_prefix_beam_amd/csrc/gr_beam_step.hip"]
 STEP_CFGS = (4, 2)            # beam-step shapes reported (900 and 128 beams)
+PAGE_SIZE = 16                # tokens per page of the paged-ContextKV measurement
 
 
 def algorithmic(inp: I.Inputs):
@@ -250,13 +251,20 @@ def write_step_profile(d, f_fetch, f_write, copy_fetch_kib, copy_write_kib):
     print(f"wrote profiles/{name}.txt", flush=True)
 
 
-def measure(cfg: int, steps: int, warmup: int):
+def measure(cfg: int, steps: int, warmup: int, page_size=None):
+    """Time gr_decode_attn on workload `cfg` (gr_decode_attn_paged with the
+    context scattered over pages of `page_size` tokens when it is given)."""
     import torch
     from shared_prefix_beam_amd import gr_attn
 
     inp = I.generate(I.WORKLOADS[cfg])
     nbytes, flops = algorithmic(inp)
     base = I.to_torch(inp)
+    if page_size:
+        pg = I.to_paged(inp, page_size, seed=cfg)
+        base["ctx_k"] = torch.from_numpy(pg.k_pages.view(np.int16)).view(torch.bfloat16).cuda()
+        base["ctx_v"] = torch.from_numpy(pg.v_pages.view(np.int16)).view(torch.bfloat16).cuda()
+        base["page_table"] = torch.from_numpy(pg.page_table.astype(np.int32)).cuda()
     footprint = sum(t.numel() * t.element_size() for t in base.values()) \
         + base["q"].numel() * 2 + base["q"].shape[0] * base["q"].shape[1] * 4
     n_sets = max(2, int(np.ceil(2 * MALL_BYTES / footprint)) + 1)
@@ -268,19 +276,40 @@ def measure(cfg: int, steps: int, warmup: int):
 
     # one front-end call per input copy validates shapes; the timed loop then
     # calls the C entry point directly with the same arguments
-    for s, (o, l) in zip(sets, outs):
-        gr_attn.decode_attn(s["q"], s["ctx_k"], s["ctx_v"], s["ctx_len"], s["beam_k"],
-                            s["beam_v"], s["beam_path"], s["beam_len"], s["row_offset"],
-                            W_max=W_max, out=o, lse=l, stream=stream)
-    dims = gr_attn.make_dims(base["q"], base["ctx_k"], base["beam_k"], base["beam_path"], W_max)
-    args = [tuple(t.data_ptr() for t in (s["row_offset"], s["q"], s["ctx_k"], s["ctx_v"],
-                                         s["ctx_len"], s["beam_k"], s["beam_v"],
-                                         s["beam_path"], s["beam_len"], o, l))
-            for s, (o, l) in zip(sets, outs)]
+    if page_size:
+        for s, (o, l) in zip(sets, outs):
+            gr_attn.decode_attn_paged(s["q"], s["ctx_k"], s["ctx_v"], s["page_table"], page_size,
+                                      s["ctx_len"], s["beam_k"], s["beam_v"], s["beam_path"],
+                                      s["beam_len"], s["row_offset"], W_max=W_max,
+                                      ctx_cap=inp.ctx_cap, out=o, lse=l, stream=stream)
+        dims = gr_attn.Dims(B=inp.B, R=inp.R, Hq=inp.wl.Hq, Hkv=inp.wl.Hkv, D=inp.wl.D,
+                            W_max=W_max, T_cap=inp.T_cap, reserved=0, ctx_cap=inp.ctx_cap,
+                            beam_cap=inp.beam_cap, scale=0.0, flags=0)
+        ctxs = [gr_attn.PagedCtx(k_pages=s["ctx_k"].data_ptr(), v_pages=s["ctx_v"].data_ptr(),
+                                 page_table=s["page_table"].data_ptr(), page_size=page_size,
+                                 pages_per_req=s["page_table"].shape[1],
+                                 n_pages=s["ctx_k"].shape[0]) for s in sets]
+        args = [tuple(t.data_ptr() for t in (s["row_offset"], s["q"], s["ctx_len"], s["beam_k"],
+                                             s["beam_v"], s["beam_path"], s["beam_len"], o, l))
+                for s, (o, l) in zip(sets, outs)]
+    else:
+        for s, (o, l) in zip(sets, outs):
+            gr_attn.decode_attn(s["q"], s["ctx_k"], s["ctx_v"], s["ctx_len"], s["beam_k"],
+                                s["beam_v"], s["beam_path"], s["beam_len"], s["row_offset"],
+                                W_max=W_max, out=o, lse=l, stream=stream)
+        dims = gr_attn.make_dims(base["q"], base["ctx_k"], base["beam_k"], base["beam_path"],
+                                 W_max)
+        args = [tuple(t.data_ptr() for t in (s["row_offset"], s["q"], s["ctx_k"], s["ctx_v"],
+                                             s["ctx_len"], s["beam_k"], s["beam_v"],
+                                             s["beam_path"], s["beam_len"], o, l))
+                for s, (o, l) in zip(sets, outs)]
     handle = stream.cuda_stream
 
     def step(i):
-        st = gr_attn.gr_decode_attn(dims, *args[i % n_sets], handle)
+        if page_size:
+            st = gr_attn.gr_decode_attn_paged(dims, ctxs[i % n_sets], *args[i % n_sets], handle)
+        else:
+            st = gr_attn.gr_decode_attn(dims, *args[i % n_sets], handle)
         if st != gr_attn.GR_OK:
             raise gr_attn.GrAttnError(st, "gr_decode_attn")
 
@@ -488,6 +517,7 @@ def main():
                      "algorithmic_bytes": prim["nbytes"]},
         "spot_check": {"max_abs": prim["spot_abs"], "lse_abs": prim["spot_lse"]},
     }
+    sec = None
     if not args.no_secondary:
         sec = measure(SECONDARY, args.steps, args.warmup)
         si = sec["inp"]
@@ -503,6 +533,18 @@ def main():
             "spot_check": {"max_abs": sec["spot_abs"], "lse_abs": sec["spot_lse"]},
         }
     line["beam_step"] = [step_entry(measure_step(c, args.steps, args.warmup)) for c in STEP_CFGS]
+    paged = []
+    for cfg, dense in ((PRIMARY, prim), (SECONDARY, sec)):
+        if dense is None:
+            continue
+        r = measure(cfg, args.steps, args.warmup, page_size=PAGE_SIZE)
+        t = r["launch_ms"] * 1e-3
+        paged.append({"workload": r["inp"].wl.name, "page_size": PAGE_SIZE,
+                      "launch_us": r["launch_ms"] * 1e3,
+                      "hbm_GBps": r["nbytes"] / t / 1e9, "TFLOPs": r["flops"] / t / 1e12,
+                      "vs_dense_launch": dense["launch_ms"] / r["launch_ms"],
+                      "spot_check": {"max_abs": r["spot_abs"], "lse_abs": r["spot_lse"]}})
+    line["paged"] = paged
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line), flush=True)
