@@ -6,6 +6,7 @@ it with gcc and marshals numpy buffers; it does no arithmetic of its own.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 from typing import Optional, Sequence
@@ -213,3 +214,44 @@ def decode_attn_paged(q, k_pages, v_pages, page_table, page_size, ctx_len, beam_
     k, v = gather_pages(k_pages, v_pages, page_table, page_size, ctx_len, ctx_cap)
     return decode_attn(q, k, v, ctx_len, beam_k, beam_v, beam_path, beam_len, row_offset,
                        scale=scale, rows=rows, n_threads=n_threads)
+
+
+def beam_select(row_offset_old, row_offset_new, score_old, logits):
+    """Beam selection of one decode step, in fp64 (xGR review, section "xBeam";
+    SID-GR README, "Roadmap": log_softmax + top-K + beam selection).
+
+    Request b's candidates are (w, v) over its old beams w and the vocabulary
+    v, with value score_old[w] + log_softmax(logits[w])[v] (natural log).  The
+    K_b = row_offset_new[b+1] - row_offset_new[b] best are kept, ordered by
+    value (larger first) and, among equal values, by the flat index w*V + v
+    (smaller first).  Returns (score_new [R_new], parent [R_new] (w within
+    the request), token [R_new]) packed like row_offset_new; a request with
+    fewer candidates than K_b fills the rest with (-inf, -1, -1).
+    """
+    row_offset_old = np.asarray(row_offset_old)
+    row_offset_new = np.asarray(row_offset_new)
+    logits = np.asarray(logits, dtype=np.float64)
+    score_old = np.asarray(score_old, dtype=np.float64)
+    B = row_offset_new.size - 1
+    V = logits.shape[1] if logits.ndim == 2 else 0
+    R_new = int(row_offset_new[-1])
+    score_new = np.full(R_new, -np.inf)
+    parent = np.full(R_new, -1, dtype=np.int32)
+    token = np.full(R_new, -1, dtype=np.int32)
+    for b in range(B):
+        r0, r1 = int(row_offset_old[b]), int(row_offset_old[b + 1])
+        k0, k1 = int(row_offset_new[b]), int(row_offset_new[b + 1])
+        if r1 == r0 or V == 0:
+            continue
+        x = logits[r0:r1]                                        # [W][V]
+        m = x.max(axis=1, keepdims=True)
+        lse = m + np.log(np.exp(x - m).sum(axis=1, keepdims=True))
+        value = (score_old[r0:r1, None] + x - lse).ravel()       # flat index w*V + v
+        flat = np.arange(value.size)
+        order = np.lexsort((flat, -value))                       # value desc, then index asc
+        n = min(k1 - k0, value.size)
+        sel = order[:n]
+        score_new[k0:k0 + n] = value[sel]
+        parent[k0:k0 + n] = sel // V
+        token[k0:k0 + n] = sel % V
+    return score_new, parent, token

@@ -390,6 +390,50 @@ def step_workload(cfg: int) -> StepInputs:
     return step_inputs(**w)
 
 
+@dataclasses.dataclass
+class SelectInputs:
+    """One beam-selection call: the previous step's beams and their next-token
+    logits, and how many beams each request keeps."""
+
+    row_offset_old: np.ndarray  # [B+1] i32
+    row_offset_new: np.ndarray  # [B+1] i32 (request b keeps W_new[b] beams)
+    score_old: np.ndarray       # [R_old] f32, cumulative log-probability of each beam
+    logits: np.ndarray          # [R_old][V] f32
+
+    @property
+    def V(self) -> int:
+        return self.logits.shape[1]
+
+
+def select_inputs(W_old: Sequence[int], W_new: Sequence[int], V: int, seed: int,
+                  logit_std: float = 2.0, score_spread: float = 3.0) -> SelectInputs:
+    """Seeded selection call: cumulative scores -|N(0, score_spread)| (log
+    probabilities), logits N(0, logit_std) in fp32; scores then logits."""
+    rng = np.random.default_rng(seed)
+    ro = np.zeros(len(W_old) + 1, dtype=np.int32)
+    ro[1:] = np.cumsum(np.asarray(W_old, dtype=np.int64))
+    rn = np.zeros(len(W_new) + 1, dtype=np.int32)
+    rn[1:] = np.cumsum(np.asarray(W_new, dtype=np.int64))
+    R = int(ro[-1])
+    score = -np.abs(rng.standard_normal(R).astype(np.float32) * np.float32(score_spread))
+    logits = rng.standard_normal((R, V), dtype=np.float32) * np.float32(logit_std)
+    return SelectInputs(row_offset_old=ro, row_offset_new=rn, score_old=score, logits=logits)
+
+
+# Beam selection at the attention workloads' widths, over an 8192-entry
+# semantic-ID vocabulary.
+SELECT_WORKLOADS = {
+    2: dict(name="w128_b8_v8192", W_old=(128,) * 8, W_new=(128,) * 8, V=8192, seed=2303),
+    4: dict(name="w900_b4_v8192", W_old=(900,) * 4, W_new=(900,) * 4, V=8192, seed=4505),
+}
+
+
+def select_workload(cfg: int) -> SelectInputs:
+    w = dict(SELECT_WORKLOADS[cfg])
+    w.pop("name")
+    return select_inputs(**w)
+
+
 def unique_beam_rows(inp: Inputs) -> List[int]:
     """Per request: number of distinct BeamKV tokens referenced by its paths."""
     out = []
