@@ -210,6 +210,51 @@ int gr_beam_step(const gr_beam_step_dims *dims, const int32_t *row_offset_old,
                  const void *new_v, int32_t *path_new, int32_t *beam_len_new, void *beam_k,
                  void *beam_v, int32_t *violations, void *stream);
 
+/* Sizes of one beam selection.  Host memory; read only during the call. */
+typedef struct gr_beam_select_dims {
+    int32_t B;        /* requests (>= 0) */
+    int32_t R_old;    /* beam rows before the step = row_offset_old[B] (>= 0) */
+    int32_t R_new;    /* beams kept = row_offset_new[B] (>= 0) */
+    int32_t V;        /* vocabulary: logits per row, 1 .. 16384 */
+    int32_t K_max;    /* upper bound on any request's kept beams, 1 .. 1024 */
+    int32_t reserved; /* must be 0 */
+} gr_beam_select_dims;
+
+/* Workspace gr_beam_select needs for these sizes (bytes, 256-byte aligned). */
+size_t gr_beam_select_workspace_bytes(const gr_beam_select_dims *dims);
+
+/*
+ * Beam selection of one decode step: log_softmax + top-K over every (beam,
+ * token) candidate of a request, with early-terminated sorting.  Sorting
+ * stops for a beam once its candidates fall below the beam width's least
+ * kept element (xGR review, section "xBeam"); log_softmax, top-K and
+ * selection run on the device (SID-GR README, "Roadmap").
+ *
+ * Request b had W_old = row_offset_old[b+1] - row_offset_old[b] beams with
+ * cumulative scores score_old (natural-log probabilities).  It keeps
+ * K_b = row_offset_new[b+1] - row_offset_new[b] <= K_max beams: the K_b best
+ * candidates (w, v), w < W_old, v < V, valued
+ *     score_old[w] + logits[w][v] - ln sum_u exp(logits[w][u])      (fp32)
+ * ranked by value (larger first) and, among equal values, by w*V + v
+ * (smaller first).  For k < K_b the packed outputs at row_offset_new[b] + k are
+ *     score_new = the value, parent = w (beam within the request), token = v,
+ * in rank order.  A request with fewer than K_b candidates (or more than
+ * K_max to keep) fills the rest with (-inf, -1, -1).  (parent, token) feed
+ * gr_beam_step and the next decode step.
+ *
+ * Layouts (DEVICE memory except dims): row_offset_old, row_offset_new int32
+ * [B+1]; score_old fp32 [R_old]; logits fp32 [R_old][V] (every row with at
+ * least one finite logit); score_new fp32 [R_new]; parent, token int32
+ * [R_new]; workspace of gr_beam_select_workspace_bytes(dims) bytes (caller-
+ * owned, not shared by concurrent calls).  Values are computed in fp32:
+ * candidates within rounding of each other may rank in either order.  Other
+ * properties as for gr_decode_attn (GR_ERR_DIMS for a short workspace).
+ */
+int gr_beam_select(const gr_beam_select_dims *dims, const int32_t *row_offset_old,
+                   const int32_t *row_offset_new, const float *score_old, const float *logits,
+                   float *score_new, int32_t *parent, int32_t *token, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *gr_status_str(int status);
 

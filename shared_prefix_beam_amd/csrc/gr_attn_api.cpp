@@ -364,6 +364,70 @@ int gr_beam_step(const gr_beam_step_dims *d, const int32_t *row_offset_old,
     return e == hipSuccess ? GR_OK : GR_ERR_LAUNCH;
 }
 
+size_t gr_beam_select_workspace_bytes(const gr_beam_select_dims *d)
+{
+    if (!d || d->R_old < 0 || d->K_max <= 0)
+        return 0;
+    const size_t half = (size_t)d->R_old * (size_t)d->K_max * sizeof(uint64_t);
+    const size_t half_al = (half + 255) & ~(size_t)255;
+    return 2 * half_al;
+}
+
+int gr_beam_select(const gr_beam_select_dims *d, const int32_t *row_offset_old,
+                   const int32_t *row_offset_new, const float *score_old, const float *logits,
+                   float *score_new, int32_t *parent, int32_t *token, void *workspace,
+                   size_t workspace_bytes, void *stream)
+{
+    if (!d)
+        return GR_ERR_NULL;
+    if (d->B < 0 || d->R_old < 0 || d->R_new < 0 || d->V <= 0 || d->K_max <= 0 ||
+        d->reserved != 0)
+        return GR_ERR_DIMS;
+    if (d->V > gr::SEL_MAX_V || d->K_max > gr::SEL_MAX_K ||
+        static_cast<int64_t>(d->R_old) * d->V > INT32_MAX)
+        return GR_ERR_UNSUPPORTED;
+    if (d->B > 0 && (!row_offset_old || !row_offset_new))
+        return GR_ERR_NULL;
+    if (d->R_old > 0 && (!score_old || !logits))
+        return GR_ERR_NULL;
+    if (d->R_new > 0 && (!score_new || !parent || !token))
+        return GR_ERR_NULL;
+    const size_t need = gr_beam_select_workspace_bytes(d);
+    if (need > 0 && !workspace)
+        return GR_ERR_NULL;
+    if (workspace_bytes < need)
+        return GR_ERR_DIMS;
+    const void *al4[] = {row_offset_old, row_offset_new, score_old, logits, score_new, parent,
+                         token};
+    for (const void *p : al4)
+        if (p && (reinterpret_cast<uintptr_t>(p) & 3u))
+            return GR_ERR_ALIGN;
+    if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return GR_ERR_ALIGN;
+    if (d->B == 0)
+        return GR_OK;
+    int st = device_ok();
+    if (st != GR_OK)
+        return st;
+    gr::SelParams p{};
+    p.row_offset_old = row_offset_old;
+    p.row_offset_new = row_offset_new;
+    p.score_old = score_old;
+    p.logits = logits;
+    p.score_new = score_new;
+    p.parent = parent;
+    p.token = token;
+    p.ws_rows = static_cast<uint64_t *>(workspace);
+    p.ws_surv = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + need / 2);
+    p.B = d->B;
+    p.R_old = d->R_old;
+    p.R_new = d->R_new;
+    p.V = d->V;
+    p.K_max = d->K_max;
+    const hipError_t e = gr::launch_beam_select(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GR_OK : GR_ERR_LAUNCH;
+}
+
 const char *gr_status_str(int status)
 {
     switch (status) {

@@ -41,6 +41,19 @@ struct StepParams {
     int64_t beam_cap;
 };
 
+// Beam selection (log_softmax + top-K over beams x vocabulary).
+constexpr int SEL_MAX_V = 16384;   // vocabulary held in registers by one workgroup
+constexpr int SEL_MAX_K = 1024;    // beams kept per request (one LDS sort)
+struct SelParams {
+    const int32_t *row_offset_old, *row_offset_new;
+    const float *score_old, *logits;
+    float *score_new;
+    int32_t *parent, *token;
+    uint64_t *ws_rows;   // [R_old][K_max] each row's best keys, descending
+    uint64_t *ws_surv;   // [R_old][K_max] survivors, per request from row_offset_old[b]*K_max
+    int B, R_old, R_new, V, K_max;
+};
+
 // Longest key list the generic comparator keeps in LDS.
 constexpr int GENERIC_MAX_KEYS = 16320;
 
@@ -56,5 +69,6 @@ hipError_t launch_fused(const Params &p, int nqt, int nks, int grid, hipStream_t
 hipError_t launch_generic(const Params &p, hipStream_t s);
 hipError_t launch_check(const MetaCheck &c, hipStream_t s);
 hipError_t launch_beam_step(const StepParams &p, hipStream_t s);
+hipError_t launch_beam_select(const SelParams &p, hipStream_t s);
 
 }  // namespace gr

@@ -26,7 +26,8 @@ GR_ERR_LAUNCH = -5
 GR_ERR_DEVICE = -6
 
 EXPORTS = ("gr_decode_attn", "gr_decode_attn_generic", "gr_decode_attn_paged",
-           "gr_check_metadata", "gr_beam_step", "gr_status_str", "gr_version")
+           "gr_check_metadata", "gr_beam_step", "gr_beam_select_workspace_bytes",
+           "gr_beam_select", "gr_status_str", "gr_version")
 
 
 class Dims(ctypes.Structure):
@@ -46,6 +47,13 @@ class StepDims(ctypes.Structure):
                 ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32), ("T_cap", ctypes.c_int32),
                 ("W_cap", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("beam_cap", ctypes.c_int64)]
+
+
+class SelectDims(ctypes.Structure):
+    """``gr_beam_select_dims`` (host memory)."""
+
+    _fields_ = [("B", ctypes.c_int32), ("R_old", ctypes.c_int32), ("R_new", ctypes.c_int32),
+                ("V", ctypes.c_int32), ("K_max", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class PagedCtx(ctypes.Structure):
@@ -86,6 +94,11 @@ def load() -> ctypes.CDLL:
         lib.gr_decode_attn_paged.restype = ctypes.c_int
         lib.gr_beam_step.argtypes = [ctypes.POINTER(StepDims)] + [P] * 13
         lib.gr_beam_step.restype = ctypes.c_int
+        SDP = ctypes.POINTER(SelectDims)
+        lib.gr_beam_select_workspace_bytes.argtypes = [SDP]
+        lib.gr_beam_select_workspace_bytes.restype = ctypes.c_size_t
+        lib.gr_beam_select.argtypes = [SDP] + [P] * 8 + [ctypes.c_size_t, P]
+        lib.gr_beam_select.restype = ctypes.c_int
         lib.gr_status_str.argtypes = [ctypes.c_int]
         lib.gr_status_str.restype = ctypes.c_char_p
         lib.gr_version.argtypes = []
@@ -127,6 +140,17 @@ def gr_beam_step(dims: StepDims, row_offset_old, row_offset_new, parent, path_ol
     return load().gr_beam_step(ctypes.byref(dims), row_offset_old, row_offset_new, parent,
                                path_old, beam_len_old, new_k, new_v, path_new, beam_len_new,
                                beam_k, beam_v, violations, stream)
+
+
+def gr_beam_select_workspace_bytes(dims: SelectDims) -> int:
+    return load().gr_beam_select_workspace_bytes(ctypes.byref(dims))
+
+
+def gr_beam_select(dims: SelectDims, row_offset_old, row_offset_new, score_old, logits,
+                   score_new, parent, token, workspace, workspace_bytes: int, stream) -> int:
+    return load().gr_beam_select(ctypes.byref(dims), row_offset_old, row_offset_new, score_old,
+                                 logits, score_new, parent, token, workspace,
+                                 int(workspace_bytes), stream)
 
 
 def gr_status_str(status: int) -> str:
@@ -325,3 +349,54 @@ def beam_step(row_offset_old, row_offset_new, parent, path_old, beam_len_old, ne
                       _ptr(violations), _stream_handle(stream))
     if st != GR_OK:
         raise GrAttnError(st, "gr_beam_step")
+
+
+def beam_select(row_offset_old, row_offset_new, score_old, logits, K_max: int, *, R_new=None,
+                score_new=None, parent=None, token=None, workspace=None, stream=None):
+    """log_softmax + top-K beam selection of one decode step (include/gr_attn.h).
+
+    ``row_offset_new`` gives every request's kept-beam count; ``K_max`` bounds
+    it and ``R_new`` (= row_offset_new[-1]) sizes the outputs when they are
+    not passed.  Returns (score_new fp32, parent int32, token int32) of
+    length R_new, enqueued on ``stream`` (default: torch's current one).
+    """
+    import torch
+    for name, t, dt in (("row_offset_old", row_offset_old, torch.int32),
+                        ("row_offset_new", row_offset_new, torch.int32),
+                        ("score_old", score_old, torch.float32),
+                        ("logits", logits, torch.float32)):
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if logits.dim() != 2:
+        raise ValueError("logits must be [R_old, V]")
+    R_old, V = logits.shape
+    B = row_offset_old.numel() - 1
+    if row_offset_new.numel() != B + 1 or score_old.numel() != R_old:
+        raise ValueError("request or row count mismatch")
+    if R_new is None:
+        if score_new is None:
+            raise ValueError("pass R_new or the output tensors")
+        R_new = score_new.numel()
+    dev = logits.device
+    if score_new is None:
+        score_new = torch.empty(R_new, dtype=torch.float32, device=dev)
+    if parent is None:
+        parent = torch.empty(R_new, dtype=torch.int32, device=dev)
+    if token is None:
+        token = torch.empty(R_new, dtype=torch.int32, device=dev)
+    for name, t, dt in (("score_new", score_new, torch.float32), ("parent", parent, torch.int32),
+                        ("token", token, torch.int32)):
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous() or t.numel() != R_new:
+            raise ValueError(f"{name} must be a contiguous device {dt} tensor of {R_new}")
+    dims = SelectDims(B=B, R_old=R_old, R_new=R_new, V=V, K_max=int(K_max), reserved=0)
+    ws_bytes = gr_beam_select_workspace_bytes(dims)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    st = gr_beam_select(dims, _ptr(row_offset_old), _ptr(row_offset_new), _ptr(score_old),
+                        _ptr(logits), _ptr(score_new), _ptr(parent), _ptr(token), _ptr(workspace),
+                        workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    if st != GR_OK:
+        raise GrAttnError(st, "gr_beam_select")
+    return score_new, parent, token

@@ -196,3 +196,75 @@ def test_paged_bad_ctx_rejected(over, code):
 def test_paged_null_ctx_rejected():
     assert gr_attn.load().gr_decode_attn_paged(ctypes.byref(good_dims()), None,
                                                *([None] * 10)) == gr_attn.GR_ERR_NULL
+
+
+# ---- gr_beam_select host validation ----------------------------------------
+def test_select_dims_struct_layout():
+    assert ctypes.sizeof(gr_attn.SelectDims) == 24
+
+
+def select_dims(**over):
+    d = dict(B=2, R_old=6, R_new=8, V=1000, K_max=5, reserved=0)
+    d.update(over)
+    return gr_attn.SelectDims(**d)
+
+
+def select_call(dims, ws_bytes=None, **ptrs):
+    args = dict(ro_old=P16, ro_new=P16, score_old=P16, logits=P16, score_new=P16, parent=P16,
+                token=P16, workspace=P16)
+    args.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = gr_attn.gr_beam_select_workspace_bytes(dims)
+    return gr_attn.gr_beam_select(dims, args["ro_old"], args["ro_new"], args["score_old"],
+                                  args["logits"], args["score_new"], args["parent"],
+                                  args["token"], args["workspace"], ws_bytes, None)
+
+
+def test_select_workspace_size():
+    # two R_old x K_max tables of 8-byte keys, each rounded up to 256 bytes
+    assert gr_attn.gr_beam_select_workspace_bytes(select_dims()) == 2 * 256
+    half = 900 * 900 * 8                      # 6480000 = 25312.5 * 256
+    assert gr_attn.gr_beam_select_workspace_bytes(select_dims(R_old=900, K_max=900)) == \
+        2 * (half + 128)
+    assert gr_attn.gr_beam_select_workspace_bytes(select_dims(R_old=0)) == 0
+    assert gr_attn.load().gr_beam_select_workspace_bytes(None) == 0
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(B=-1), gr_attn.GR_ERR_DIMS),
+    (dict(R_old=-1), gr_attn.GR_ERR_DIMS),
+    (dict(R_new=-1), gr_attn.GR_ERR_DIMS),
+    (dict(V=0), gr_attn.GR_ERR_DIMS),
+    (dict(K_max=0), gr_attn.GR_ERR_DIMS),
+    (dict(reserved=1), gr_attn.GR_ERR_DIMS),
+    (dict(V=16385), gr_attn.GR_ERR_UNSUPPORTED),
+    (dict(K_max=1025), gr_attn.GR_ERR_UNSUPPORTED),
+    (dict(R_old=200000, V=16384), gr_attn.GR_ERR_UNSUPPORTED),
+])
+def test_select_bad_dims_rejected(over, code):
+    assert select_call(select_dims(**over), ws_bytes=1 << 40) == code
+
+
+@pytest.mark.parametrize("which", ["ro_old", "ro_new", "score_old", "logits", "score_new",
+                                   "parent", "token", "workspace"])
+def test_select_null_pointer_rejected(which):
+    assert select_call(select_dims(), **{which: None}) == gr_attn.GR_ERR_NULL
+
+
+def test_select_null_dims_rejected():
+    assert gr_attn.load().gr_beam_select(None, *([None] * 8), 0, None) == gr_attn.GR_ERR_NULL
+
+
+def test_select_short_workspace_rejected():
+    d = select_dims()
+    assert select_call(d, ws_bytes=gr_attn.gr_beam_select_workspace_bytes(d) - 1) == \
+        gr_attn.GR_ERR_DIMS
+
+
+@pytest.mark.parametrize("which,off", [("logits", 2), ("token", 1), ("workspace", 8)])
+def test_select_misaligned_rejected(which, off):
+    assert select_call(select_dims(), **{which: P16 + off}) == gr_attn.GR_ERR_ALIGN
+
+
+def test_select_empty_batch_is_a_no_op():
+    assert select_call(select_dims(B=0, R_old=0, R_new=0)) == gr_attn.GR_OK

@@ -1,0 +1,187 @@
+"""GPU parity of beam selection (log_softmax + top-K over beams x vocabulary)
+through the C ABI against the fp64 oracle.
+
+The device ranks fp32 values and the oracle fp64 ones, so candidates whose
+values lie within rounding of each other may legitimately swap.  The checks:
+every device score equals the oracle's value of the same (parent, token)
+within TOL; ranks whose oracle value is separated from both neighbours by
+more than 2*TOL hold exactly the oracle's candidate; the device set is a
+top-K within 2*TOL (nothing left out beats anything kept by more than that);
+the device order is by its own score, then flat index; padding is exact.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import log
+from oracle import oracle as O
+from shared_prefix_beam_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+# fp32 value = score + logit - LSE with |value| < 64: a few ulp (4e-6 each)
+# from the additions, plus the fp32 log-sum-exp's relative error (sum of up to
+# 16384 terms in a 256-thread tree, fast exp/log) amplified by nothing: the
+# LSE enters additively.  1e-4 leaves a factor >10 of margin.
+TOL = 1e-4
+MARGIN = 64
+
+
+def run_gpu(si, K_max):
+    import torch
+    from shared_prefix_beam_amd import gr_attn
+    dev = "cuda"
+    R_new = int(si.row_offset_new[-1])
+    out = gr_attn.beam_select(torch.from_numpy(si.row_offset_old).to(dev),
+                              torch.from_numpy(si.row_offset_new).to(dev),
+                              torch.from_numpy(si.score_old).to(dev),
+                              torch.from_numpy(np.ascontiguousarray(si.logits)).to(dev),
+                              K_max, R_new=R_new)
+    torch.cuda.synchronize()
+    return tuple(t.cpu().numpy() for t in out)
+
+
+def check_against_oracle(si, gpu, K_max, what):
+    score, parent, token = gpu
+    ro, rn = si.row_offset_old, si.row_offset_new
+    B, V = len(ro) - 1, si.V
+    W = np.diff(ro).astype(np.int64)
+    K = np.diff(rn).astype(np.int64)
+    # the oracle's best K + MARGIN of every request
+    wide = np.minimum(K + MARGIN, W * V)
+    rw = np.zeros(B + 1, dtype=np.int64)
+    rw[1:] = np.cumsum(wide)
+    o_score, o_parent, o_token = O.beam_select(ro, rw, si.score_old, si.logits)
+    for b in range(B):
+        k0, k1 = int(rn[b]), int(rn[b + 1])
+        n_real = int(min(K[b], K_max, W[b] * V))
+        g_s, g_p, g_t = score[k0:k1], parent[k0:k1], token[k0:k1]
+        tag = f"{what} request {b} (W={W[b]}, K={K[b]})"
+        # padding
+        assert np.all(g_s[n_real:] == -np.inf) and np.all(g_p[n_real:] == -1) \
+            and np.all(g_t[n_real:] == -1), f"{tag}: padding"
+        if n_real == 0:
+            continue
+        g_s, g_p, g_t = g_s[:n_real], g_p[:n_real], g_t[:n_real]
+        assert np.all((g_p >= 0) & (g_p < W[b]) & (g_t >= 0) & (g_t < V)), f"{tag}: range"
+        g_flat = g_p.astype(np.int64) * V + g_t
+        assert np.unique(g_flat).size == n_real, f"{tag}: repeated candidate"
+        # device order: score descending, then flat index ascending
+        assert np.all(g_s[1:] <= g_s[:-1]), f"{tag}: scores not descending"
+        eq = g_s[1:] == g_s[:-1]                  # -inf == -inf counts as a tie
+        assert np.all(np.diff(g_flat)[eq] > 0), f"{tag}: tie order"
+        # oracle values of the device's candidates
+        w0, w1 = int(rw[b]), int(rw[b + 1])
+        o_flat = o_parent[w0:w1].astype(np.int64) * V + o_token[w0:w1]
+        o_val = o_score[w0:w1]
+        pos = {int(f): i for i, f in enumerate(o_flat)}
+        missing = [int(f) for f in g_flat if int(f) not in pos]
+        assert not missing, f"{tag}: {len(missing)} device picks outside the oracle's best " \
+                            f"{w1 - w0}"
+        idx = np.array([pos[int(f)] for f in g_flat])
+        u = o_val[idx]
+        fin = np.isfinite(u)
+        assert np.array_equal(np.isfinite(g_s), fin), f"{tag}: -inf mismatch"
+        err = np.abs(g_s[fin].astype(np.float64) - u[fin])
+        assert err.size == 0 or err.max() <= TOL, f"{tag}: score error {err.max():.3g}"
+        # a top-K within 2*TOL: what the oracle keeps and the device drops
+        # is no better than the device's worst pick by more than that
+        dropped = np.setdiff1d(np.arange(n_real), idx)
+        if dropped.size:
+            assert o_val[dropped].max() <= u.min() + 2 * TOL, f"{tag}: set"
+        # separated ranks are unique: exact match there
+        ext = np.concatenate([[np.inf], o_val, [-np.inf]])
+        with np.errstate(invalid="ignore"):       # inf - inf: not separated
+            gap_hi = ext[:-2][:n_real] - o_val[:n_real]
+            gap_lo = o_val[:n_real] - ext[2:][:n_real]
+        sep = (gap_hi > 2 * TOL) & (gap_lo > 2 * TOL)
+        assert np.array_equal(g_flat[sep], o_flat[:n_real][sep]), f"{tag}: rank mismatch"
+        log(f"  {tag}: {int(sep.sum())}/{n_real} ranks separated and equal, "
+            f"max err {0 if err.size == 0 else err.max():.2e}")
+
+
+def select_case(W_old, W_new, V, seed, K_max=None, **kw):
+    si = I.select_inputs(W_old, W_new, V, seed, **kw)
+    K_max = K_max if K_max is not None else max(max(W_new), 1)
+    return si, K_max
+
+
+def test_ragged_small():
+    """Ragged requests: no old beams, no kept beams, fewer rows than K (no
+    bound), one row, V not a multiple of the 256-thread tile."""
+    si, K_max = select_case([3, 0, 7, 1, 5, 2], [4, 2, 0, 9, 5, 40], V=300, seed=1)
+    log("[select] ragged small")
+    check_against_oracle(si, run_gpu(si, K_max), K_max, "ragged")
+
+
+def test_fewer_candidates_than_kept():
+    """W*V < K: every candidate is kept, then (-inf, -1, -1) padding."""
+    si, K_max = select_case([1, 2], [9, 7], V=3, seed=2)
+    log("[select] fewer candidates than kept")
+    check_against_oracle(si, run_gpu(si, K_max), K_max, "short")
+
+
+def test_vocabulary_of_one():
+    si, K_max = select_case([4, 3], [2, 3], V=1, seed=3)
+    log("[select] V=1")
+    check_against_oracle(si, run_gpu(si, K_max), K_max, "V=1")
+
+
+def test_kept_beyond_k_max_is_padded():
+    """A request keeping more than K_max beams gets the best K_max, then
+    padding (the documented clamp)."""
+    si = I.select_inputs([5, 6], [3, 9], V=50, seed=4)
+    log("[select] K > K_max clamp")
+    check_against_oracle(si, run_gpu(si, 6), 6, "clamp")
+
+
+def test_exact_ties_break_by_index():
+    """Logits on a coarse grid: many exact ties inside a row, ranked by token
+    index on both sides."""
+    si = I.select_inputs([6, 9], [40, 25], V=700, seed=5)
+    si.logits = np.round(si.logits * 2) / 2
+    si.score_old[:] = np.float32(-1.0)
+    log("[select] exact ties")
+    check_against_oracle(si, run_gpu(si, 40), 40, "ties")
+
+
+def test_masked_vocabulary():
+    """Most logits -inf (a constrained vocabulary): finite candidates first,
+    then -inf ones by flat index once the finite ones run out."""
+    si = I.select_inputs([4, 3], [30, 200], V=500, seed=6)
+    rng = np.random.default_rng(7)
+    mask = rng.random(si.logits.shape) < 0.9
+    mask[:, 0] = False                            # every row keeps a finite logit
+    si.logits[mask] = -np.inf
+    log("[select] masked vocabulary")
+    check_against_oracle(si, run_gpu(si, 200), 200, "masked")
+
+
+def test_many_rows_few_kept():
+    """W much larger than K: the bound comes from the rows' heads."""
+    si, K_max = select_case([2000, 700], [4, 1], V=1000, seed=8)
+    log("[select] many rows, few kept")
+    check_against_oracle(si, run_gpu(si, K_max), K_max, "wide")
+
+
+def test_maximum_sizes():
+    """V = 16384 and K = K_max = 1024, beside a small request."""
+    si = I.select_inputs([1100, 3], [1024, 17], V=16384, seed=9)
+    log("[select] V=16384, K=1024")
+    check_against_oracle(si, run_gpu(si, 1024), 1024, "max")
+
+
+@pytest.mark.parametrize("cfg", sorted(I.SELECT_WORKLOADS))
+def test_select_workloads(cfg):
+    """The benchmarked shapes (W=128 x 8 requests, W=900 x 4, V=8192)."""
+    si = I.select_workload(cfg)
+    log(f"[select] workload {I.SELECT_WORKLOADS[cfg]['name']}")
+    K_max = int(np.diff(si.row_offset_new).max())
+    check_against_oracle(si, run_gpu(si, K_max), K_max, I.SELECT_WORKLOADS[cfg]["name"])
+
+
+def test_repeatable():
+    """Two calls on the same inputs give bitwise-equal outputs."""
+    si, K_max = select_case([128] * 3, [128] * 3, V=4096, seed=10)
+    a, b = run_gpu(si, K_max), run_gpu(si, K_max)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.int32), y.view(np.int32))
