@@ -43,6 +43,9 @@ KERNEL_SOURCES = ["shared_prefix_beam_amd/csrc/gr_attn_kernels.hip",
                   "shared_prefix_beam_amd/csrc/gr_attn_api.cpp"]
 STEP_SOURCES = ["shared_prefix_beam_amd/csrc/gr_beam_step.hip"]
 STEP_CFGS = (4, 2)            # beam-step shapes reported (900 and 128 beams)
+SELECT_SOURCES = ["shared_prefix_beam_amd/csrc/gr_beam_select.hip"]
+SELECT_CFGS = (4, 2)          # beam-selection shapes reported (900 and 128 beams)
+SELECT_KERNELS = ("select_rows", "select_request")
 PAGE_SIZE = 16                # tokens per page of the paged-ContextKV measurement
 
 
@@ -81,6 +84,16 @@ def algorithmic_step(st: I.StepInputs) -> int:
         t = int(s.beam_len[b])
         nbytes += w_new * (4 * row + 4 + 4 * t + 4 * (t + 1)) + 16
     return nbytes
+
+
+def algorithmic_select(si: I.SelectInputs) -> int:
+    """Bytes one beam selection must move, each once: every logit and old
+    score read, the two row-offset arrays read, and (score, parent, token)
+    written per kept beam."""
+    R_old, V = si.logits.shape
+    B = si.row_offset_old.size - 1
+    R_new = int(si.row_offset_new[-1])
+    return 4 * R_old * V + 4 * R_old + 8 * (B + 1) + 12 * R_new
 
 
 def kernel_hash(sources=None) -> str:
@@ -413,6 +426,82 @@ def measure_step(cfg: int, steps: int, warmup: int):
                 n_sets=n_sets, bit_exact=bool(ok))
 
 
+def measure_select(cfg: int, steps: int, warmup: int):
+    """Time gr_beam_select on the selection workload `cfg` (both launches of
+    one call between one event pair), rotating input sets like `measure`."""
+    import torch
+    from shared_prefix_beam_amd import gr_attn
+
+    si = I.select_workload(cfg)
+    nbytes = algorithmic_select(si)
+    R_old, V = si.logits.shape
+    B = si.row_offset_old.size - 1
+    R_new = int(si.row_offset_new[-1])
+    K_max = int(np.diff(si.row_offset_new).max())
+    dev = "cuda"
+    base = dict(ro_old=torch.from_numpy(si.row_offset_old).to(dev),
+                ro_new=torch.from_numpy(si.row_offset_new).to(dev),
+                score_old=torch.from_numpy(si.score_old).to(dev),
+                logits=torch.from_numpy(np.ascontiguousarray(si.logits)).to(dev))
+    n_sets = max(2, int(np.ceil(2 * MALL_BYTES / nbytes)) + 1)
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(n_sets - 1)]
+    score_new = torch.empty(R_new, dtype=torch.float32, device=dev)
+    parent = torch.empty(R_new, dtype=torch.int32, device=dev)
+    token = torch.empty(R_new, dtype=torch.int32, device=dev)
+    dims = gr_attn.SelectDims(B=B, R_old=R_old, R_new=R_new, V=V, K_max=K_max, reserved=0)
+    ws_bytes = gr_attn.gr_beam_select_workspace_bytes(dims)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for t in sets:   # the front end validates every set once
+        gr_attn.beam_select(t["ro_old"], t["ro_new"], t["score_old"], t["logits"], K_max,
+                            score_new=score_new, parent=parent, token=token, workspace=ws,
+                            stream=stream)
+    order = ("ro_old", "ro_new", "score_old", "logits")
+    args = [tuple(t[k].data_ptr() for k in order) for t in sets]
+    outs = (score_new.data_ptr(), parent.data_ptr(), token.data_ptr(), ws.data_ptr(), ws_bytes)
+    handle = stream.cuda_stream
+
+    def call(i):
+        rc = gr_attn.gr_beam_select(dims, *args[i % n_sets], *outs, handle)
+        if rc != gr_attn.GR_OK:
+            raise gr_attn.GrAttnError(rc, "gr_beam_select")
+
+    for i in range(warmup):
+        call(i)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(steps):
+        call(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    launch_ms = ev0.elapsed_time(ev1) / steps
+    # spot check against the oracle (not timed): the last call used set
+    # (steps - 1) % n_sets, identical to the first
+    from oracle import oracle as O
+    o_s, o_p, o_t = O.beam_select(si.row_offset_old, si.row_offset_new, si.score_old, si.logits)
+    g_s, g_p, g_t = (x.cpu().numpy() for x in (score_new, parent, token))
+    same = (g_p == o_p) & (g_t == o_t)
+    err = float(np.abs(g_s[same].astype(np.float64) - o_s[same]).max()) if same.any() else None
+    return dict(si=si, name=I.SELECT_WORKLOADS[cfg]["name"], nbytes=nbytes, launch_ms=launch_ms,
+                n_sets=n_sets, R_new=R_new, rank_match=float(same.mean()), max_abs=err)
+
+
+def select_entry(r) -> dict:
+    gbs = r["nbytes"] / (r["launch_ms"] * 1e-3) / 1e9
+    return {"workload": r["name"], "rows_in": int(r["si"].logits.shape[0]),
+            "beams_kept": r["R_new"], "launch_us": r["launch_ms"] * 1e3,
+            "value": r["R_new"] / (r["launch_ms"] * 1e-3), "unit": "beams-selected/s",
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS,
+                         "traffic": recorded_traffic(r["name"], "beam_select", SELECT_SOURCES),
+                         "kernel": "beam_select (select_rows + select_request)",
+                         "algorithmic_bytes": r["nbytes"]},
+            "input_copies_rotated": r["n_sets"],
+            "spot_check": {"rank_match": r["rank_match"], "max_abs": r["max_abs"]}}
+
+
 def step_entry(r) -> dict:
     gbs = r["nbytes"] / (r["launch_ms"] * 1e-3) / 1e9
     return {"workload": r["name"], "rows": r["st"].R_new, "launch_us": r["launch_ms"] * 1e3,
@@ -450,7 +539,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--only", choices=["primary", "secondary", "beam_step"],
+    ap.add_argument("--only", choices=["primary", "secondary", "beam_step", "select"],
                     help="time one workload only and print its launch time (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run 10 device copies of 256 MiB (reference for HBM byte counters)")
@@ -478,6 +567,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": 256 << 20, "launches": 10}), flush=True)
+        return
+    if args.only == "select":
+        r = measure_select(SELECT_CFGS[0], args.steps, args.warmup)
+        print(json.dumps({"workload": r["name"], "launch_us": r["launch_ms"] * 1e3,
+                          "rank_match": r["rank_match"]}), flush=True)
         return
     if args.only == "beam_step":
         r = measure_step(STEP_CFGS[0], args.steps, args.warmup)
@@ -533,6 +627,8 @@ def main():
             "spot_check": {"max_abs": sec["spot_abs"], "lse_abs": sec["spot_lse"]},
         }
     line["beam_step"] = [step_entry(measure_step(c, args.steps, args.warmup)) for c in STEP_CFGS]
+    line["beam_select"] = [select_entry(measure_select(c, args.steps, args.warmup))
+                           for c in SELECT_CFGS]
     paged = []
     for cfg, dense in ((PRIMARY, prim), (SECONDARY, sec)):
         if dense is None:

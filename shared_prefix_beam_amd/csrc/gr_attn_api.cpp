@@ -368,9 +368,7 @@ size_t gr_beam_select_workspace_bytes(const gr_beam_select_dims *d)
 {
     if (!d || d->R_old < 0 || d->K_max <= 0)
         return 0;
-    const size_t half = (size_t)d->R_old * (size_t)d->K_max * sizeof(uint64_t);
-    const size_t half_al = (half + 255) & ~(size_t)255;
-    return 2 * half_al;
+    return gr::beam_select_workspace(d->R_old, d->K_max);
 }
 
 int gr_beam_select(const gr_beam_select_dims *d, const int32_t *row_offset_old,
@@ -417,8 +415,18 @@ int gr_beam_select(const gr_beam_select_dims *d, const int32_t *row_offset_old,
     p.score_new = score_new;
     p.parent = parent;
     p.token = token;
-    p.ws_rows = static_cast<uint64_t *>(workspace);
-    p.ws_surv = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + need / 2);
+    {
+        auto al = [](size_t n) { return (n + 255) & ~(size_t)255; };
+        char *w = static_cast<char *>(workspace);
+        const size_t R = static_cast<size_t>(d->R_old);
+        p.ws_list = reinterpret_cast<uint64_t *>(w);
+        w += al(R * gr::SEL_LIST * sizeof(uint64_t));
+        p.ws_off = reinterpret_cast<float *>(w);
+        w += al(R * sizeof(float));
+        p.ws_ovf = reinterpret_cast<int32_t *>(w);
+        w += al(R * sizeof(int32_t));
+        p.ws_surv = reinterpret_cast<uint64_t *>(w);
+    }
     p.B = d->B;
     p.R_old = d->R_old;
     p.R_new = d->R_new;

@@ -43,16 +43,21 @@ struct StepParams {
 
 // Beam selection (log_softmax + top-K over beams x vocabulary).
 constexpr int SEL_MAX_V = 16384;   // vocabulary held in registers by one workgroup
-constexpr int SEL_MAX_K = 1024;    // beams kept per request (one LDS sort)
+constexpr int SEL_MAX_K = 1024;    // beams kept per request (one sort in registers)
+constexpr int SEL_LIST = 32;       // best keys kept per row for the request stage
 struct SelParams {
     const int32_t *row_offset_old, *row_offset_new;
     const float *score_old, *logits;
     float *score_new;
     int32_t *parent, *token;
-    uint64_t *ws_rows;   // [R_old][K_max] each row's best keys, descending
+    uint64_t *ws_list;   // [R_old][SEL_LIST] each row's best keys, descending
+    float *ws_off;       // [R_old] score_old - LSE of each row
+    int32_t *ws_ovf;     // [R_old] rows to select again, per request from row_offset_old[b]
     uint64_t *ws_surv;   // [R_old][K_max] survivors, per request from row_offset_old[b]*K_max
     int B, R_old, R_new, V, K_max;
 };
+// Workspace bytes of the four tables above (each 256-byte aligned).
+size_t beam_select_workspace(int R_old, int K_max);
 
 // Longest key list the generic comparator keeps in LDS.
 constexpr int GENERIC_MAX_KEYS = 16320;

@@ -10,17 +10,17 @@
 // values come first and, among equal values, smaller indices.
 //
 // gfx950 mapping, two launches:
-//  1. select_rows: one 256-thread workgroup per beam row holds the row's
-//     logits in registers, reduces its max and log-sum-exp, and selects the
-//     row's K best keys (K = beams its request keeps) with a radix select over
-//     8-bit digits (LDS histograms, one wave finding the digit), then sorts
-//     them with a bitonic network in LDS and writes them to the workspace.
+//  1. select_rows: one 256-thread workgroup per beam row reads the row's
+//     logits once into registers, reduces max and log-sum-exp, and keeps the
+//     row's L = min(K, 32) best keys, sorted.  The L-th best of the 256
+//     thread maxima bounds the row's L-th best key from below, so the radix
+//     select (8-bit digits, LDS histograms) only sees the few keys above it.
 //  2. select_request: one 1024-thread workgroup per request.  The K-th best
-//     of the rows' best keys bounds the K-th best candidate from below (when
-//     the request has at least K rows); each row's sorted list is cut where it
-//     falls below that bound (binary search: the early termination), the
-//     survivors are gathered, and the exact K best are selected among them,
-//     sorted, decoded and written.
+//     of the rows' 8 best keys bounds the request's K-th best candidate from
+//     below; every row's list is cut at that bound (the early termination),
+//     and a row whose whole list clears it while it has more candidates is
+//     selected again from its logits.  The exact K best of the survivors
+//     (held in LDS) are selected, sorted in registers and written.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,7 +30,12 @@ namespace gr {
 
 constexpr int SEL_ROW_THREADS = 256;
 constexpr int SEL_REQ_THREADS = 1024;
-constexpr int SEL_HEAD = 8;            // keys per row that set the pruning bound
+constexpr int SEL_HEAD = 8;                               // keys per row behind the bound
+constexpr int SEL_HEAD_REG = 8;                           // head keys per thread in registers
+constexpr int SEL_SURV_REG = 4;                           // survivors per thread in registers
+constexpr int SEL_SURV_LDS = SEL_SURV_REG * SEL_REQ_THREADS;
+constexpr int SEL_REQ_NV = SEL_MAX_V / SEL_REQ_THREADS;   // logits per thread, re-selection
+constexpr int SEL_CAND = SEL_ROW_THREADS;                 // keys >= the row bound kept in LDS
 
 __device__ __forceinline__ uint32_t ord_f32(float f)
 {
@@ -43,19 +48,51 @@ __device__ __forceinline__ float unord_f32(uint32_t o)
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
-__device__ __forceinline__ uint64_t make_key(float value, uint32_t flat)
+__device__ __forceinline__ uint64_t make_key(uint32_t ord, uint32_t flat)
 {
-    return ((uint64_t)ord_f32(value) << 32) | (uint32_t)~flat;
+    return ((uint64_t)ord << 32) | (uint32_t)~flat;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m)
+{
+    const uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Value of lane (lane ^ J) for J in {1, 2, 4, 8}, through DPP moves (VALU,
+// no LDS traffic): quad permutations for 1 and 2; for 4 and 8 a row shift
+// up (lane + J) or down (lane - J), picked by the lane's bit J.
+template <int J>
+__device__ __forceinline__ uint32_t dpp_xor_u32(uint32_t v)
+{
+    const int x = (int)v;
+    if constexpr (J == 1) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);
+    } else if constexpr (J == 2) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);
+    } else {
+        const int up = __builtin_amdgcn_update_dpp(0, x, 0x100 + J, 0xF, 0xF, false);
+        const int dn = __builtin_amdgcn_update_dpp(0, x, 0x110 + J, 0xF, 0xF, false);
+        return (uint32_t)((threadIdx.x & J) ? dn : up);
+    }
+}
+
+template <int J>
+__device__ __forceinline__ uint64_t dpp_xor_u64(uint64_t v)
+{
+    const uint32_t lo = dpp_xor_u32<J>((uint32_t)v), hi = dpp_xor_u32<J>((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
 }
 
 // Largest and smallest 64-bit key over the block (every thread passes its
-// own; threads with no key pass kmax = 0, kmin = ~0).
+// own; threads with no key pass kmax = 0, kmin = ~0).  One barrier; `red`
+// may be written again only after a later barrier.
 template <int NT>
 __device__ void block_minmax(uint64_t &kmax, uint64_t &kmin, uint64_t *red)
 {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     for (int off = 32; off > 0; off >>= 1) {
-        const uint64_t a = __shfl_xor(kmax, off), c = __shfl_xor(kmin, off);
+        const uint64_t a = shfl_xor_u64(kmax, off), c = shfl_xor_u64(kmin, off);
         kmax = a > kmax ? a : kmax;
         kmin = c < kmin ? c : kmin;
     }
@@ -71,22 +108,67 @@ __device__ void block_minmax(uint64_t &kmax, uint64_t &kmin, uint64_t *red)
         kmax = red[2 * w] > kmax ? red[2 * w] : kmax;
         kmin = red[2 * w + 1] < kmin ? red[2 * w + 1] : kmin;
     }
+}
+
+// Sum over the block; one barrier, `red` reusable after a later barrier.
+template <int NT>
+__device__ int block_sum(int v, int *red)
+{
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    for (int off = 32; off > 0; off >>= 1)
+        v += __shfl_xor(v, off);
+    if (lane == 0)
+        red[wv] = v;
     __syncthreads();
+    v = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w)
+        v += red[w];
+    return v;
+}
+
+// Inclusive prefix sum over the threads in order, and the total.  One
+// barrier; `wsum` reusable after a later barrier.
+template <int NT>
+__device__ int block_incl_scan(int v, int *wsum, int &total)
+{
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(v, off);
+        if (lane >= off)
+            v += t;
+    }
+    if (lane == 63)
+        wsum[wv] = v;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        const int s = wsum[w];
+        before += w < wv ? s : 0;
+        total += s;
+    }
+    return v + before;
 }
 
 // Threshold of the k-th largest of n distinct keys lying in [kmin, kmax], as
 // (prefix, mask): the k largest keys are exactly those with (key & mask) >=
 // prefix.  The bits kmin and kmax share are shared by every key and decided
-// at once; the rest are resolved 8 bits per pass from the top (LDS histogram,
-// one wave finding the digit where the count from the top reaches k), and
-// the passes stop once every key of the chosen bin is needed.  visit(f)
-// calls f(key) for each key the calling thread owns.  Requires 1 <= k <= n;
-// all NT threads call it.
+// at once; the rest are resolved 8 bits per pass from the top.  Each pass
+// counts the keys still matching into a 256-bin LDS histogram; after one
+// barrier every wave reads it and finds the digit where the count from the
+// top reaches k.  The passes stop once every key of the chosen bin is
+// needed.  Three histograms rotate (hist3, 3 x 256): on entry
+// hist3[256*hbuf ..] is zero and published by a barrier; on exit hbuf names
+// the one zeroed by the last pass.  visit(f) calls f(key) for each key the
+// calling thread owns.  Requires 1 <= k <= n; all NT threads call it.
 template <int NT, class Visit>
-__device__ void radix_kth(int k, uint64_t kmax, uint64_t kmin, Visit visit, uint32_t *hist,
-                          int *st, uint64_t &prefix_out, uint64_t &mask_out)
+__device__ void radix_kth(int k, uint64_t kmax, uint64_t kmin, Visit visit, uint32_t *hist3,
+                          int &hbuf, uint64_t &prefix_out, uint64_t &mask_out)
 {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
     const uint64_t diff = kmax ^ kmin;
     const int common = diff ? __clzll(diff) : 64;
     uint64_t mask = common == 0 ? 0 : (~0ull << (64 - common));
@@ -94,53 +176,54 @@ __device__ void radix_kth(int k, uint64_t kmax, uint64_t kmin, Visit visit, uint
     int hi = 64 - common;                    // bits [0, hi) still undecided
     int remaining = k;
     while (hi > 0) {
+        uint32_t *h = hist3 + 256 * hbuf;
+        const int nb = hbuf == 2 ? 0 : hbuf + 1;
+        uint32_t *hn = hist3 + 256 * nb;
+        for (int i = tid; i < 256; i += NT)
+            hn[i] = 0;                            // the histogram of the next pass
         const int lo = hi > 8 ? hi - 8 : 0;
         const uint32_t dmask = (1u << (hi - lo)) - 1u;
-        for (int i = tid; i < 256; i += NT)
-            hist[i] = 0;
-        __syncthreads();
         visit([&](uint64_t key) {
             if ((key & mask) == prefix)
-                atomicAdd(&hist[(uint32_t)(key >> lo) & dmask], 1u);
+                atomicAdd(&h[(uint32_t)(key >> lo) & dmask], 1u);
         });
         __syncthreads();
-        if (tid < 64) {
-            // lane l holds bins 4l .. 4l+3; suffix sums over lanes find the
-            // bin where the count from the top reaches `remaining`
-            const int lane = tid;
-            uint32_t b[4];
+        // lane l holds bins 4l .. 4l+3; suffix sums over lanes find the bin
+        // where the count from the top reaches `remaining`
+        uint32_t b[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                b[j] = hist[4 * lane + j];
-            const uint32_t own = b[0] + b[1] + b[2] + b[3];
-            uint32_t suf = own;
+        for (int j = 0; j < 4; ++j)
+            b[j] = h[4 * lane + j];
+        const uint32_t own = b[0] + b[1] + b[2] + b[3];
+        uint32_t suf = own;
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const uint32_t t = __shfl_down(suf, off);
-                if (lane + off < 64)
-                    suf += t;
-            }
-            const uint32_t above_lane = suf - own;
-            if (suf >= (uint32_t)remaining && above_lane < (uint32_t)remaining) {
-                uint32_t cum = above_lane;
-                for (int j = 3; j >= 0; --j) {
-                    if (cum + b[j] >= (uint32_t)remaining || j == 0) {
-                        st[0] = 4 * lane + j;
-                        st[1] = (int)cum;
-                        st[2] = (int)b[j];
-                        break;
-                    }
-                    cum += b[j];
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t t = __shfl_down(suf, off);
+            if (lane + off < 64)
+                suf += t;
+        }
+        const uint32_t above_lane = suf - own;
+        const bool here = suf >= (uint32_t)remaining && above_lane < (uint32_t)remaining;
+        int d_l = 0, above_l = 0, cnt_l = 0;
+        if (here) {
+            uint32_t cum = above_lane;
+            for (int j = 3; j >= 0; --j) {
+                if (cum + b[j] >= (uint32_t)remaining || j == 0) {
+                    d_l = 4 * lane + j;
+                    above_l = (int)cum;
+                    cnt_l = (int)b[j];
+                    break;
                 }
+                cum += b[j];
             }
         }
-        __syncthreads();
-        const int d = st[0], above = st[1], cnt = st[2];
-        __syncthreads();                          // st and hist are reused next pass
+        const int src = __ffsll((unsigned long long)__ballot(here)) - 1;
+        const int d = __shfl(d_l, src), above = __shfl(above_l, src), cnt = __shfl(cnt_l, src);
         prefix |= (uint64_t)d << lo;
         mask |= (uint64_t)dmask << lo;
         remaining -= above;
         hi = lo;
+        hbuf = nb;
         if (cnt == remaining)
             break;
     }
@@ -164,27 +247,44 @@ __device__ __forceinline__ int wave_append(bool take, int *counter)
     return base + __popcll(ballot & ((1ull << lane) - 1ull));
 }
 
-// Bitonic sort of buf[0 .. ns) into descending order (ns a power of two).
+// Bitonic sort of one key per thread into descending order over threads
+// 0 .. ns-1 (ns a power of two <= NT; threads from ns on hold 0).  Stages
+// with partners 1, 2, 4, 8 lanes away exchange through DPP, 16 and 32
+// through lane shuffles, wider ones through one of two LDS buffers in turn
+// (xch2: 2 x NT keys), one barrier each.
 template <int NT>
-__device__ void block_sort_desc(uint64_t *buf, int ns)
+__device__ uint64_t block_sort_desc(uint64_t key, int ns, uint64_t *xch2)
 {
     const int tid = threadIdx.x;
+    int buf = 0;
     for (int k = 2; k <= ns; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < ns; i += NT) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const uint64_t a = buf[i], c = buf[ixj];
-                    const bool desc = (i & k) == 0;
-                    if (desc ? (a < c) : (a > c)) {
-                        buf[i] = c;
-                        buf[ixj] = a;
-                    }
-                }
+            uint64_t other;
+            if (j >= 64) {
+                uint64_t *x = xch2 + NT * buf;
+                x[tid] = key;
+                __syncthreads();
+                other = x[tid ^ j];
+                buf ^= 1;
+            } else if (j == 1) {
+                other = dpp_xor_u64<1>(key);
+            } else if (j == 2) {
+                other = dpp_xor_u64<2>(key);
+            } else if (j == 4) {
+                other = dpp_xor_u64<4>(key);
+            } else if (j == 8) {
+                other = dpp_xor_u64<8>(key);
+            } else {
+                other = shfl_xor_u64(key, j);
             }
-            __syncthreads();
+            const bool desc = (tid & k) == 0;     // this block of k sorts descending
+            const bool lower = (tid & j) == 0;    // lower index of its pair
+            const uint64_t big = key > other ? key : other;
+            const uint64_t small = key > other ? other : key;
+            key = (lower == desc) ? big : small;
         }
     }
+    return key;
 }
 
 __device__ __forceinline__ int pow2_at_least(int n)
@@ -213,11 +313,15 @@ __device__ __forceinline__ int request_of(const int32_t *row_offset, int B, int 
 template <int NV>
 __global__ __launch_bounds__(SEL_ROW_THREADS) void select_rows(const SelParams p)
 {
-    __shared__ uint32_t hist[256];
-    __shared__ int st[4];
-    __shared__ float red[SEL_ROW_THREADS / 64];
-    __shared__ uint64_t red64[2 * SEL_ROW_THREADS / 64];
-    __shared__ uint64_t buf[SEL_MAX_K];
+    constexpr int NT = SEL_ROW_THREADS, NW = NT / 64;
+    __shared__ float red[NW];
+    __shared__ int wsum[NW];
+    __shared__ uint64_t tq[NW];
+    __shared__ uint64_t cand[SEL_CAND];
+    __shared__ uint64_t red64[2 * NW];
+    // used only when many keys tie around the bound
+    __shared__ uint32_t hist3[3 * 256];
+    __shared__ uint64_t buf[SEL_LIST];
     __shared__ int n_buf;
 
     const int r = blockIdx.x;
@@ -230,12 +334,13 @@ __global__ __launch_bounds__(SEL_ROW_THREADS) void select_rows(const SelParams p
     k_row = k_row < p.K_max ? k_row : p.K_max;
     if (k_row <= 0)
         return;
+    const int L = k_row < SEL_LIST ? k_row : SEL_LIST;
 
     const float *row = p.logits + (int64_t)r * p.V;
     float x[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int v = tid + SEL_ROW_THREADS * i;
+        const int v = tid + NT * i;
         x[i] = v < p.V ? row[v] : -__builtin_huge_valf();
     }
     // max and log-sum-exp over the row
@@ -250,7 +355,7 @@ __global__ __launch_bounds__(SEL_ROW_THREADS) void select_rows(const SelParams p
     __syncthreads();
     m = red[0];
 #pragma unroll
-    for (int w = 1; w < SEL_ROW_THREADS / 64; ++w)
+    for (int w = 1; w < NW; ++w)
         m = __builtin_fmaxf(m, red[w]);
     __syncthreads();
     float s = 0.f;
@@ -264,65 +369,125 @@ __global__ __launch_bounds__(SEL_ROW_THREADS) void select_rows(const SelParams p
     __syncthreads();
     s = 0.f;
 #pragma unroll
-    for (int w = 0; w < SEL_ROW_THREADS / 64; ++w)
+    for (int w = 0; w < NW; ++w)
         s += red[w];
     const float off_w = p.score_old[r] - (m + __logf(s));
+    if (tid == 0)
+        p.ws_off[r] = off_w;
 
     // the candidates' ordered value bits replace the logits
     uint32_t o[NV];
-    uint64_t kmax = 0, kmin = ~0ull;
     const uint32_t flat0 = (uint32_t)wl * (uint32_t)p.V + (uint32_t)tid;
+    const bool has = tid < p.V;
+    uint64_t tmax = 0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         o[i] = ord_f32(off_w + x[i]);
-        if (tid + SEL_ROW_THREADS * i < p.V) {
-            const uint64_t key = ((uint64_t)o[i] << 32) | ~(flat0 + SEL_ROW_THREADS * i);
-            kmax = key > kmax ? key : kmax;
-            kmin = key < kmin ? key : kmin;
+        if (tid + NT * i < p.V) {
+            const uint64_t key = make_key(o[i], flat0 + NT * i);
+            tmax = key > tmax ? key : tmax;
         }
     }
-    block_minmax<SEL_ROW_THREADS>(kmax, kmin, red64);
-    auto visit = [&](auto f) {
+    // t0: when every thread holds keys (V >= NT), each wave's q-th best
+    // thread maximum (q = ceil(L / NW)), found bit by bit with ballots,
+    // bounds q distinct keys of the wave from below, and the smallest of the
+    // NW bounds L distinct keys; otherwise t0 = 0 (fewer than NT keys)
+    uint64_t t0 = 0;
+    if (p.V >= NT) {
+        const int q = (L + NW - 1) / NW;
+        uint64_t res = 0;
+        for (int bit = 63; bit >= 0; --bit) {
+            const uint64_t cand_bits = res | (1ull << bit);
+            if (__popcll(__ballot(tmax >= cand_bits)) >= q)
+                res = cand_bits;
+        }
+        if (lane == 0)
+            tq[wv] = res;
+        __syncthreads();
+        t0 = tq[0];
 #pragma unroll
-        for (int i = 0; i < NV; ++i)
-            if (tid + SEL_ROW_THREADS * i < p.V)
-                f(((uint64_t)o[i] << 32) | ~(flat0 + SEL_ROW_THREADS * i));
-    };
-    uint64_t prefix, mask;
-    radix_kth<SEL_ROW_THREADS>(k_row, kmax, kmin, visit, hist, st, prefix, mask);
-
-    // gather the k_row selected keys, sort them, write the row's list
+        for (int w = 1; w < NW; ++w)
+            t0 = tq[w] < t0 ? tq[w] : t0;
+    }
+    // the keys >= t0, compacted in thread order
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+        c += (tid + NT * i < p.V && make_key(o[i], flat0 + NT * i) >= t0) ? 1 : 0;
+    int M;
+    const int incl = block_incl_scan<NT>(c, wsum, M);
+    if (M <= SEL_CAND) {
+        int at = incl - c;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const uint64_t key = make_key(o[i], flat0 + NT * i);
+            if (tid + NT * i < p.V && key >= t0)
+                cand[at++] = key;
+        }
+        __syncthreads();
+        // rank among the candidates: the L best land in the row's list in order
+        if (tid < M) {
+            const uint64_t mine = cand[tid];
+            int rk = 0;
+            for (int j = 0; j < M; ++j)
+                rk += cand[j] > mine ? 1 : 0;
+            if (rk < L)
+                p.ws_list[(int64_t)r * SEL_LIST + rk] = mine;
+        }
+        return;
+    }
+    // many keys at or above t0: radix select of the L best among them
+    hist3[tid] = 0;                               // NT == 256 bins
+    uint64_t best = tmax, unused = ~0ull;
+    block_minmax<NT>(best, unused, red64);        // its barrier publishes hist3
+    int hb = 0;
+    uint64_t pf, mk;
+    radix_kth<NT>(
+        L, best, t0,
+        [&](auto f) {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const uint64_t key = make_key(o[i], flat0 + NT * i);
+                if (tid + NT * i < p.V && key >= t0)
+                    f(key);
+            }
+        },
+        hist3, hb, pf, mk);
     if (tid == 0)
         n_buf = 0;
-    const int ns = pow2_at_least(k_row);
-    for (int i = tid; i < ns; i += SEL_ROW_THREADS)
-        buf[i] = 0;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const uint64_t key = ((uint64_t)o[i] << 32) | ~(flat0 + SEL_ROW_THREADS * i);
-        const bool take = tid + SEL_ROW_THREADS * i < p.V && (key & mask) >= prefix;
+        const uint64_t key = make_key(o[i], flat0 + NT * i);
+        const bool take = tid + NT * i < p.V && key >= t0 && (key & mk) >= pf;
         const int at = wave_append(take, &n_buf);
-        if (take && at < k_row)
+        if (take && at < L)
             buf[at] = key;
     }
     __syncthreads();
-    block_sort_desc<SEL_ROW_THREADS>(buf, ns);
-    uint64_t *dst = p.ws_rows + (int64_t)r * p.K_max;
-    for (int i = tid; i < k_row; i += SEL_ROW_THREADS)
-        dst[i] = buf[i];
+    if (tid < L) {
+        const uint64_t mine = buf[tid];
+        int rk = 0;
+        for (int j = 0; j < L; ++j)
+            rk += buf[j] > mine ? 1 : 0;
+        p.ws_list[(int64_t)r * SEL_LIST + rk] = mine;
+    }
 }
 
 __global__ __launch_bounds__(SEL_REQ_THREADS) void select_request(const SelParams p)
 {
-    constexpr int NW = SEL_REQ_THREADS / 64;
-    __shared__ uint32_t hist[256];
-    __shared__ int st[4];
-    __shared__ uint64_t red64[2 * NW];
-    __shared__ int scan[SEL_REQ_THREADS];
-    __shared__ uint64_t buf[SEL_MAX_K];
-    __shared__ int n_buf;
-    __shared__ int carry;
+    constexpr int NT = SEL_REQ_THREADS, NW = NT / 64;
+    constexpr int WROWS = 32;                           // rows per wave and chunk
+    constexpr int CHUNK = WROWS * NW;
+    constexpr int RPL = 64 / (SEL_LIST / 2);            // rows per wave-wide 16-byte load
+    constexpr int LOADS = WROWS / RPL;
+    __shared__ uint32_t hist3[3 * 256];
+    __shared__ uint64_t red64a[2 * NW], red64b[2 * NW];
+    __shared__ int redi[NW], wsum[NW];
+    __shared__ int cnt_lds[NT];
+    __shared__ uint64_t xch2[2 * NT];
+    __shared__ uint64_t surv_lds[SEL_SURV_LDS];
+    __shared__ int n_sel, n_ovf;
 
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
@@ -338,131 +503,295 @@ __global__ __launch_bounds__(SEL_REQ_THREADS) void select_request(const SelParam
         return;
     int k_row = K < p.V ? K : p.V;
     k_row = k_row < p.K_max ? k_row : p.K_max;
+    const int L = k_row < SEL_LIST ? k_row : SEL_LIST;
+    const int head = L < SEL_HEAD ? L : SEL_HEAD;
     const int K_eff = K < p.K_max ? K : p.K_max;      // keys that can be produced
-    const uint64_t *rows = p.ws_rows + (int64_t)r0 * p.K_max;
-
-    // Lower bound of the K-th best candidate: the K-th best among the first
-    // `head` keys of every row (distinct candidates).  Keys below it cannot
-    // be among the K best; without K head keys there is no bound.
-    const int head = k_row < SEL_HEAD ? k_row : SEL_HEAD;
-    const int n_head = W * head;
-    uint64_t tau = 0;
-    if (W > 0 && n_head >= K_eff) {
-        auto head_key = [&](int i) { return rows[(int64_t)(i / head) * p.K_max + i % head]; };
-        uint64_t kmax = 0, kmin = ~0ull;
-        for (int i = tid; i < n_head; i += SEL_REQ_THREADS) {
-            const uint64_t key = head_key(i);
-            kmax = key > kmax ? key : kmax;
-            kmin = key < kmin ? key : kmin;
-        }
-        block_minmax<SEL_REQ_THREADS>(kmax, kmin, red64);
-        uint64_t pf, mk;
-        radix_kth<SEL_REQ_THREADS>(
-            K_eff, kmax, kmin,
-            [&](auto f) {
-                for (int i = tid; i < n_head; i += SEL_REQ_THREADS)
-                    f(head_key(i));
-            },
-            hist, st, pf, mk);
-        // the K_eff selected head keys are all >= pf
-        tau = pf;
-    }
-    // survivors: the prefix of each row's sorted list at or above tau (the
-    // early termination of that row's candidates)
+    const uint64_t *lists = p.ws_list + (int64_t)r0 * SEL_LIST;
     uint64_t *surv = p.ws_surv + (int64_t)r0 * p.K_max;
+    int32_t *ovf_rows = p.ws_ovf + r0;
+    if (tid < 256)
+        hist3[tid] = 0;
     if (tid == 0)
-        carry = 0;
+        n_ovf = 0;
     __syncthreads();
-    for (int base = 0; base < W; base += SEL_REQ_THREADS) {
-        const int w = base + tid;
-        int c = 0;
-        if (w < W) {
-            const uint64_t *lst = rows + (int64_t)w * p.K_max;
-            int lo = 0, hi = k_row;              // count of keys >= tau in a descending list
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (lst[mid] >= tau)
-                    lo = mid + 1;
-                else
-                    hi = mid;
-            }
-            c = lo;
-        }
-        scan[tid] = c;
-        __syncthreads();
-        for (int off = 1; off < SEL_REQ_THREADS; off <<= 1) {   // inclusive scan
-            const int t = tid >= off ? scan[tid - off] : 0;
-            __syncthreads();
-            scan[tid] += t;
-            __syncthreads();
-        }
-        // one wave copies one row's survivors
-        const int n_rows = W - base < SEL_REQ_THREADS ? W - base : SEL_REQ_THREADS;
-        for (int j = wv; j < n_rows; j += NW) {
-            const int end = scan[j];
-            const int cj = end - (j ? scan[j - 1] : 0);
-            const uint64_t *lst = rows + (int64_t)(base + j) * p.K_max;
-            uint64_t *out = surv + carry + end - cj;
-            for (int i = lane; i < cj; i += 64)
-                out[i] = lst[i];
-        }
-        __syncthreads();
-        if (tid == SEL_REQ_THREADS - 1)
-            carry += scan[tid];
-        __syncthreads();
-    }
-    const int N = carry;
+    int hb = 0;
 
-    // exact best K_eff among the N survivors, sorted
-    const int take = K_eff < N ? K_eff : N;
-    uint64_t pf = 0, mk = 0;
-    if (take > 0) {
+    // Lists of a chunk of CHUNK rows: wave wv reads rows wv*WROWS .. of the
+    // chunk with 16-byte lanes (keys 2kp, 2kp+1 of row g of each load), RPL
+    // rows per load.  The first chunk stays in registers for steps 1 and 2.
+    const int g = lane / (SEL_LIST / 2), kp = lane % (SEL_LIST / 2);
+    uint64_t ka[LOADS], kb[LOADS];
+    auto load_chunk = [&](int base, int rows_here) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int rl = wv * WROWS + i * RPL + g;
+            ka[i] = kb[i] = 0;
+            if (rl < rows_here && 2 * kp < L) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(
+                    lists + (int64_t)(base + rl) * SEL_LIST + 2 * kp);
+                ka[i] = ((uint64_t)v.y << 32) | v.x;
+                kb[i] = ((uint64_t)v.w << 32) | v.z;
+            }
+        }
+    };
+    load_chunk(0, W < CHUNK ? W : CHUNK);
+
+    // 1. Lower bound tau of the K-th best candidate: the K-th best among the
+    //    first `head` keys of every row (distinct candidates).  Without K
+    //    head keys there is no bound.
+    uint64_t tau = 0;
+    const int n_head = W * head;
+    if (W > 0 && n_head >= K_eff) {
+        // heads: from the chunk in registers when it holds every row, else
+        // loaded into SEL_HEAD_REG registers per thread, else streamed
+        auto head_key = [&](int i) { return lists[(int64_t)(i / head) * SEL_LIST + i % head]; };
+        const int mode = W <= CHUNK ? 0 : (n_head <= SEL_HEAD_REG * NT ? 1 : 2);
+        uint64_t hk[SEL_HEAD_REG];
+        if (mode == 1) {
+#pragma unroll
+            for (int j = 0; j < SEL_HEAD_REG; ++j) {
+                const int i = tid + NT * j;
+                hk[j] = i < n_head ? head_key(i) : 0;
+            }
+        }
+        auto visit = [&](auto f) {
+            if (mode == 0) {
+#pragma unroll
+                for (int i = 0; i < LOADS; ++i) {
+                    if (wv * WROWS + i * RPL + g < W) {
+                        if (2 * kp < head)
+                            f(ka[i]);
+                        if (2 * kp + 1 < head)
+                            f(kb[i]);
+                    }
+                }
+            } else if (mode == 1) {
+#pragma unroll
+                for (int j = 0; j < SEL_HEAD_REG; ++j)
+                    if (tid + NT * j < n_head)
+                        f(hk[j]);
+            } else {
+                for (int i = tid; i < n_head; i += NT)
+                    f(head_key(i));
+            }
+        };
         uint64_t kmax = 0, kmin = ~0ull;
-        for (int i = tid; i < N; i += SEL_REQ_THREADS) {
-            const uint64_t key = surv[i];
+        visit([&](uint64_t key) {
             kmax = key > kmax ? key : kmax;
             kmin = key < kmin ? key : kmin;
+        });
+        block_minmax<NT>(kmax, kmin, red64a);
+        uint64_t pf, mk;
+        radix_kth<NT>(K_eff, kmax, kmin, visit, hist3, hb, pf, mk);
+        tau = pf;                                   // the K_eff selected keys are >= pf
+    }
+
+    // 2. Survivors: each row's list entries >= tau (a prefix: the lists are
+    //    sorted); a row's count is the popcount of its lanes in two ballots.
+    //    A row whose whole list clears tau while it has more candidates is
+    //    selected again below.
+    int N = 0;
+    for (int base = 0; base < W; base += CHUNK) {
+        const int rows_here = W - base < CHUNK ? W - base : CHUNK;
+        if (base > 0)
+            load_chunk(base, rows_here);
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int rl = wv * WROWS + i * RPL + g;
+            const bool in = rl < rows_here;
+            const uint64_t ba = __ballot(in && 2 * kp < L && ka[i] >= tau);
+            const uint64_t bb = __ballot(in && 2 * kp + 1 < L && kb[i] >= tau);
+            const int sh = (SEL_LIST / 2) * g;
+            const uint64_t gm = (1ull << (SEL_LIST / 2)) - 1ull;
+            const int c = __popcll((ba >> sh) & gm) + __popcll((bb >> sh) & gm);
+            if (kp == 0 && in) {
+                const bool ovf = c == L && L < k_row;
+                cnt_lds[rl] = ovf ? 0 : c;
+                if (ovf)
+                    ovf_rows[atomicAdd(&n_ovf, 1)] = base + rl;
+            }
         }
-        block_minmax<SEL_REQ_THREADS>(kmax, kmin, red64);
-        radix_kth<SEL_REQ_THREADS>(
+        __syncthreads();
+        int tot;
+        const int incl = block_incl_scan<NT>(tid < rows_here ? cnt_lds[tid] : 0, wsum, tot);
+        __syncthreads();                            // every count read
+        if (tid < rows_here)
+            cnt_lds[tid] = incl;                    // end of the row's survivors
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int rl = wv * WROWS + i * RPL + g;
+            if (rl < rows_here) {
+                const int end = cnt_lds[rl];
+                const int c = end - (rl ? cnt_lds[rl - 1] : 0);
+                const int at = N + end - c + 2 * kp;
+                if (2 * kp < c) {
+                    surv[at] = ka[i];
+                    if (at < SEL_SURV_LDS)
+                        surv_lds[at] = ka[i];
+                }
+                if (2 * kp + 1 < c) {
+                    surv[at + 1] = kb[i];
+                    if (at + 1 < SEL_SURV_LDS)
+                        surv_lds[at + 1] = kb[i];
+                }
+            }
+        }
+        N += tot;
+        __syncthreads();                            // cnt_lds and wsum reused
+    }
+    const int n_over = n_ovf;
+
+    // 3. Rows selected again from their logits: every key >= tau competes,
+    //    the row's k_row best of them are appended.
+    for (int j = 0; j < n_over; ++j) {
+        const int w = ovf_rows[j];
+        const int r = r0 + w;
+        const float off_w = p.ws_off[r];
+        const float *row = p.logits + (int64_t)r * p.V;
+        const uint32_t flat0 = (uint32_t)w * (uint32_t)p.V + (uint32_t)tid;
+        uint32_t o[SEL_REQ_NV];
+        uint64_t kmax = 0, kmin = ~0ull;
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < SEL_REQ_NV; ++i) {
+            const int v = tid + NT * i;
+            o[i] = v < p.V ? ord_f32(off_w + row[v]) : 0;
+            const uint64_t key = make_key(o[i], flat0 + NT * i);
+            if (v < p.V && key >= tau) {
+                kmax = key > kmax ? key : kmax;
+                kmin = key < kmin ? key : kmin;
+                ++cnt;
+            }
+        }
+        const int M = block_sum<NT>(cnt, redi);
+        block_minmax<NT>(kmax, kmin, red64b);
+        const int take = k_row < M ? k_row : M;     // M >= L >= 1: the list's keys
+        uint64_t pf, mk;
+        auto visit = [&](auto f) {
+#pragma unroll
+            for (int i = 0; i < SEL_REQ_NV; ++i) {
+                const uint64_t key = make_key(o[i], flat0 + NT * i);
+                if (tid + NT * i < p.V && key >= tau)
+                    f(key);
+            }
+        };
+        radix_kth<NT>(take, kmax, kmin, visit, hist3, hb, pf, mk);
+        if (tid == 0)
+            n_sel = 0;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < SEL_REQ_NV; ++i) {
+            const uint64_t key = make_key(o[i], flat0 + NT * i);
+            const bool sel = tid + NT * i < p.V && key >= tau && (key & mk) >= pf;
+            const int at = wave_append(sel, &n_sel);
+            if (sel && at < take)
+                surv[N + at] = key;
+        }
+        __syncthreads();                            // n_sel, redi and red64b reused
+        N += take;
+    }
+
+    // 4. The K_eff best survivors, sorted, decoded and written.  Up to NT
+    //    survivors are sorted as they are; more are first cut to the K_eff
+    //    best by a radix select.
+    const bool from_lds = n_over == 0 && N <= SEL_SURV_LDS;
+    const uint64_t *sv = from_lds ? surv_lds : surv;
+    const int take = K_eff < N ? K_eff : N;
+    uint64_t key = 0;
+    int ns = 1;
+    if (N <= NT) {
+        key = tid < N ? sv[tid] : 0;
+        ns = pow2_at_least(N > 0 ? N : 1);
+    } else {
+        uint64_t pf = 0, mk = 0;
+        const bool in_reg = N <= SEL_SURV_REG * NT;
+        uint64_t sk[SEL_SURV_REG];
+        uint64_t kmax = 0, kmin = ~0ull;
+        if (in_reg) {
+#pragma unroll
+            for (int j = 0; j < SEL_SURV_REG; ++j) {
+                const int i = tid + NT * j;
+                sk[j] = i < N ? sv[i] : 0;
+                if (i < N) {
+                    kmax = sk[j] > kmax ? sk[j] : kmax;
+                    kmin = sk[j] < kmin ? sk[j] : kmin;
+                }
+            }
+        } else {
+            for (int i = tid; i < N; i += NT) {
+                const uint64_t k2 = sv[i];
+                kmax = k2 > kmax ? k2 : kmax;
+                kmin = k2 < kmin ? k2 : kmin;
+            }
+        }
+        block_minmax<NT>(kmax, kmin, red64a);
+        radix_kth<NT>(
             take, kmax, kmin,
             [&](auto f) {
-                for (int i = tid; i < N; i += SEL_REQ_THREADS)
-                    f(surv[i]);
+                if (in_reg) {
+#pragma unroll
+                    for (int j = 0; j < SEL_SURV_REG; ++j)
+                        if (tid + NT * j < N)
+                            f(sk[j]);
+                } else {
+                    for (int i = tid; i < N; i += NT)
+                        f(sv[i]);
+                }
             },
-            hist, st, pf, mk);
-    }
-    if (tid == 0)
-        n_buf = 0;
-    const int ns = pow2_at_least(take > 0 ? take : 1);
-    for (int i = tid; i < ns; i += SEL_REQ_THREADS)
-        buf[i] = 0;
-    __syncthreads();
-    if (take > 0) {
-        for (int base = 0; base < N; base += SEL_REQ_THREADS) {
-            const int i = base + tid;
-            const uint64_t key = i < N ? surv[i] : 0;
-            const bool sel = i < N && (key & mk) >= pf;
-            const int at = wave_append(sel, &n_buf);
-            if (sel && at < take)
-                buf[at] = key;
-        }
-    }
-    __syncthreads();
-    block_sort_desc<SEL_REQ_THREADS>(buf, ns);
-    for (int i = tid; i < K; i += SEL_REQ_THREADS) {
-        if (i < take) {
-            const uint64_t key = buf[i];
-            const uint32_t flat = ~(uint32_t)key;
-            p.score_new[k0 + i] = unord_f32((uint32_t)(key >> 32));
-            p.parent[k0 + i] = (int)(flat / (uint32_t)p.V);
-            p.token[k0 + i] = (int)(flat % (uint32_t)p.V);
+            hist3, hb, pf, mk);
+        if (tid == 0)
+            n_sel = 0;
+        __syncthreads();
+        if (in_reg) {
+#pragma unroll
+            for (int j = 0; j < SEL_SURV_REG; ++j) {
+                const bool sel = tid + NT * j < N && (sk[j] & mk) >= pf;
+                const int at = wave_append(sel, &n_sel);
+                if (sel && at < take)
+                    xch2[at] = sk[j];
+            }
         } else {
-            p.score_new[k0 + i] = -__builtin_huge_valf();
-            p.parent[k0 + i] = -1;
-            p.token[k0 + i] = -1;
+            for (int base = 0; base < N; base += NT) {
+                const int i = base + tid;
+                const uint64_t k2 = i < N ? sv[i] : 0;
+                const bool sel = i < N && (k2 & mk) >= pf;
+                const int at = wave_append(sel, &n_sel);
+                if (sel && at < take)
+                    xch2[at] = k2;
+            }
+        }
+        __syncthreads();
+        key = tid < take ? xch2[tid] : 0;           // take <= K_max <= NT
+        ns = pow2_at_least(take);
+    }
+    __syncthreads();                                // xch2 is the sort's exchange
+    key = block_sort_desc<NT>(key, ns, xch2);
+    if (tid < K) {
+        if (tid < take) {
+            const uint32_t flat = ~(uint32_t)key;
+            p.score_new[k0 + tid] = unord_f32((uint32_t)(key >> 32));
+            p.parent[k0 + tid] = (int)(flat / (uint32_t)p.V);
+            p.token[k0 + tid] = (int)(flat % (uint32_t)p.V);
+        } else {
+            p.score_new[k0 + tid] = -__builtin_huge_valf();
+            p.parent[k0 + tid] = -1;
+            p.token[k0 + tid] = -1;
         }
     }
+    for (int i = tid + NT; i < K; i += NT) {        // kept beyond K_max: padding
+        p.score_new[k0 + i] = -__builtin_huge_valf();
+        p.parent[k0 + i] = -1;
+        p.token[k0 + i] = -1;
+    }
+}
+
+size_t beam_select_workspace(int R_old, int K_max)
+{
+    auto al = [](size_t n) { return (n + 255) & ~(size_t)255; };
+    const size_t R = static_cast<size_t>(R_old);
+    return al(R * SEL_LIST * sizeof(uint64_t)) + al(R * sizeof(float)) +
+           al(R * sizeof(int32_t)) + al(R * static_cast<size_t>(K_max) * sizeof(uint64_t));
 }
 
 hipError_t launch_beam_select(const SelParams &p, hipStream_t s)

@@ -221,11 +221,15 @@ def select_call(dims, ws_bytes=None, **ptrs):
 
 
 def test_select_workspace_size():
-    # two R_old x K_max tables of 8-byte keys, each rounded up to 256 bytes
-    assert gr_attn.gr_beam_select_workspace_bytes(select_dims()) == 2 * 256
-    half = 900 * 900 * 8                      # 6480000 = 25312.5 * 256
-    assert gr_attn.gr_beam_select_workspace_bytes(select_dims(R_old=900, K_max=900)) == \
-        2 * (half + 128)
+    # per row: a 32-key list (8 bytes each), its fp32 offset, an int32 slot and
+    # K_max survivor keys; four tables, each rounded up to 256 bytes
+    def al(n):
+        return (n + 255) // 256 * 256
+
+    for R, K in ((6, 5), (900, 900), (1, 1024)):
+        want = al(R * 32 * 8) + al(R * 4) + al(R * 4) + al(R * K * 8)
+        assert gr_attn.gr_beam_select_workspace_bytes(select_dims(R_old=R, K_max=K)) == want
+    assert gr_attn.gr_beam_select_workspace_bytes(select_dims(R_old=900, K_max=900)) == 6718208
     assert gr_attn.gr_beam_select_workspace_bytes(select_dims(R_old=0)) == 0
     assert gr_attn.load().gr_beam_select_workspace_bytes(None) == 0
 

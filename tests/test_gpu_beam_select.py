@@ -185,3 +185,25 @@ def test_repeatable():
     a, b = run_gpu(si, K_max), run_gpu(si, K_max)
     for x, y in zip(a, b):
         assert np.array_equal(x.view(np.int32), y.view(np.int32))
+
+
+def test_dominant_rows_are_selected_again():
+    """Two rows far above the rest: their whole 32-key lists clear the bound,
+    so they are selected again from their logits, and every kept beam comes
+    from them."""
+    si = I.select_inputs([50, 9], [200, 3], V=1000, seed=11)
+    si.score_old[:50] = np.float32(-60.0)
+    si.score_old[[7, 31]] = np.float32(0.0)
+    log("[select] dominant rows")
+    gpu = run_gpu(si, 200)
+    check_against_oracle(si, gpu, 200, "dominant")
+    assert set(np.unique(gpu[1][:200]).tolist()) == {7, 31}
+
+
+def test_no_bound_many_survivors():
+    """Fewer head keys than kept beams (no bound): every row is selected
+    again and the survivors (127 x 1024) exceed what the workgroup keeps in
+    LDS and registers."""
+    si = I.select_inputs([127], [1024], V=2000, seed=12)
+    log("[select] no bound, many survivors")
+    check_against_oracle(si, run_gpu(si, 1024), 1024, "nobound")
