@@ -1,7 +1,12 @@
-"""ctypes front end of the fp64 C oracle (``oracle.c``).  Test infrastructure only.
+"""The oracle: plain, slow, fp64 CPU definitions of what the device path
+computes.  Test infrastructure only (tests, the smoke check and the CPU
+baseline of the benchmark use it; the library never does).
 
-The C source states the definition it computes.  This wrapper only compiles
-it with gcc and marshals numpy buffers; it does no arithmetic of its own.
+Decode attention and the beam step are written in C (``oracle.c``, which
+states the definitions); this module compiles that with gcc and marshals
+numpy buffers for them.  Beam selection, the paged-context gather and the
+trie-constrained selection are written here in numpy, each citing the
+passage it follows.
 """
 from __future__ import annotations
 
@@ -255,3 +260,79 @@ def beam_select(row_offset_old, row_offset_new, score_old, logits):
         parent[k0:k0 + n] = sel // V
         token[k0:k0 + n] = sel % V
     return score_new, parent, token
+
+
+def trie_walk(node_ptr, edge_tok, edge_child, prefix) -> int:
+    """Node reached from the root by following `prefix` token by token in a
+    CSR trie (node u's children: edges node_ptr[u] .. node_ptr[u+1]-1, edge e
+    labelled edge_tok[e], leading to edge_child[e]); -1 once a token has no
+    edge (GR-Inference blog, kernel design: prefix traversal of the SID trie).
+    Each level scans all of the node's edges."""
+    node = 0
+    for t in prefix:
+        lo, hi = int(node_ptr[node]), int(node_ptr[node + 1])
+        hit = np.nonzero(np.asarray(edge_tok[lo:hi]) == int(t))[0]
+        if hit.size == 0:
+            return -1
+        node = int(edge_child[lo + int(hit[0])])
+    return node
+
+
+def beam_select_trie(row_offset_old, row_offset_new, score_old, logits, sid, node_ptr,
+                     edge_tok, edge_child):
+    """Item-constrained beam selection of one decode step, in fp64
+    (GR-Inference blog, kernel design: the item-constrained kernel does
+    prefix traversal, legal-token gather and local top-K over the SID trie;
+    xGR review, section "xBeam").
+
+    Beam w of request b holds the token prefix sid[w]; its legal next tokens
+    are the labels of the edges leaving the node that prefix reaches (none if
+    the prefix leaves the trie).  Candidate (w, t), t legal, is valued
+    score_old[w] + logits[w][t] - ln sum_{legal u} exp(logits[w][u]): the
+    log-softmax over the legal tokens only, i.e. with every other logit masked
+    to -inf.  Ranking, packing and padding as beam_select.  Returns
+    (score_new, parent, token, node_new), node_new the node of the kept
+    beam's extended prefix (-1 for padding).
+    """
+    row_offset_old = np.asarray(row_offset_old)
+    row_offset_new = np.asarray(row_offset_new)
+    logits = np.asarray(logits, dtype=np.float64)
+    score_old = np.asarray(score_old, dtype=np.float64)
+    B = row_offset_new.size - 1
+    V = logits.shape[1] if logits.ndim == 2 else 0
+    R_new = int(row_offset_new[-1])
+    score_new = np.full(R_new, -np.inf)
+    parent = np.full(R_new, -1, dtype=np.int32)
+    token = np.full(R_new, -1, dtype=np.int32)
+    node_new = np.full(R_new, -1, dtype=np.int32)
+    for b in range(B):
+        r0, r1 = int(row_offset_old[b]), int(row_offset_old[b + 1])
+        k0, k1 = int(row_offset_new[b]), int(row_offset_new[b + 1])
+        vals, flats, kids = [], [], []
+        for w in range(r1 - r0):
+            node = trie_walk(node_ptr, edge_tok, edge_child, sid[r0 + w])
+            if node < 0:
+                continue
+            lo, hi = int(node_ptr[node]), int(node_ptr[node + 1])
+            if hi == lo:
+                continue
+            legal = np.asarray(edge_tok[lo:hi], dtype=np.int64)
+            x = logits[r0 + w, legal]
+            m = x.max()
+            lse = m + np.log(np.exp(x - m).sum())
+            vals.append(score_old[r0 + w] + x - lse)
+            flats.append(w * V + legal)
+            kids.append(np.asarray(edge_child[lo:hi]))
+        if not vals:
+            continue
+        value = np.concatenate(vals)
+        flat = np.concatenate(flats)
+        kid = np.concatenate(kids)
+        order = np.lexsort((flat, -value))                       # value desc, then index asc
+        n = min(k1 - k0, value.size)
+        sel = order[:n]
+        score_new[k0:k0 + n] = value[sel]
+        parent[k0:k0 + n] = flat[sel] // V
+        token[k0:k0 + n] = flat[sel] % V
+        node_new[k0:k0 + n] = kid[sel]
+    return score_new, parent, token, node_new

@@ -460,3 +460,159 @@ def to_torch(inp: Inputs, device="cuda"):
     return dict(q=bf(inp.q), ctx_k=bf(inp.ctx_k), ctx_v=bf(inp.ctx_v), ctx_len=i32(inp.ctx_len),
                 beam_k=bf(inp.beam_k), beam_v=bf(inp.beam_v), beam_path=i32(inp.beam_path),
                 beam_len=i32(inp.beam_len), row_offset=i32(inp.row_offset))
+
+
+# ---- item catalog and its semantic-ID trie (constrained selection) ----------
+@dataclasses.dataclass
+class SidTrie:
+    """A catalog of items, each a sequence of `depth` semantic-ID tokens in
+    [0, V), and its prefix trie in CSR form (GR-Inference blog, kernel design:
+    the SID trie kept in device memory as CSR).
+
+    Node 0 is the root (the empty prefix); the nodes of prefix length d are
+    numbered after those of length d-1, in lexicographic order of their
+    prefixes.  Node u's children are edges node_ptr[u] .. node_ptr[u+1]-1,
+    edge e carrying token edge_tok[e] (increasing within a node) to node
+    edge_child[e]."""
+
+    items: np.ndarray       # [N][depth] i32, distinct, lexicographically sorted
+    node_ptr: np.ndarray    # [n_nodes + 1] i32
+    edge_tok: np.ndarray    # [n_edges] i32
+    edge_child: np.ndarray  # [n_edges] i32
+    level_start: np.ndarray  # [depth + 2] i32: nodes of prefix length d are level_start[d] ..
+    V: int
+
+    @property
+    def n_nodes(self) -> int:
+        return int(self.node_ptr.size - 1)
+
+    @property
+    def n_edges(self) -> int:
+        return int(self.edge_tok.size)
+
+    def node_of(self, prefixes: np.ndarray) -> np.ndarray:
+        """Node ids of prefixes [n][d] taken from the catalog (all of one
+        length d); -1 for a prefix no item has."""
+        prefixes = np.asarray(prefixes, dtype=np.int64).reshape(len(prefixes), -1)
+        d = prefixes.shape[1]
+        if d == 0:
+            return np.zeros(len(prefixes), dtype=np.int32)
+        codes = _prefix_codes(self.items[:, :d], self.V)
+        uniq = np.unique(codes)
+        q = _prefix_codes(prefixes, self.V)
+        pos = np.searchsorted(uniq, q)
+        pos_c = np.minimum(pos, uniq.size - 1)
+        found = (pos < uniq.size) & (uniq[pos_c] == q)
+        return np.where(found, self.level_start[d] + pos_c, -1).astype(np.int32)
+
+
+def _prefix_codes(p: np.ndarray, V: int) -> np.ndarray:
+    code = np.zeros(p.shape[0], dtype=np.int64)
+    for j in range(p.shape[1]):
+        code = code * V + p[:, j].astype(np.int64)
+    return code
+
+
+def sid_catalog(n_items: int, depth: int, V: int, seed: int) -> np.ndarray:
+    """`n_items` distinct items of `depth` tokens, uniform in [0, V), sorted."""
+    rng = np.random.default_rng(seed)
+    items = rng.integers(0, V, size=(int(n_items * 1.05) + 16, depth), dtype=np.int64)
+    items = np.unique(items, axis=0)
+    if items.shape[0] > n_items:
+        keep = np.sort(rng.choice(items.shape[0], size=n_items, replace=False))
+        items = items[keep]
+    return items.astype(np.int32)
+
+
+def build_trie(items: np.ndarray, V: int) -> SidTrie:
+    """CSR prefix trie of distinct, lexicographically sorted items."""
+    items = np.asarray(items, dtype=np.int32)
+    depth = items.shape[1]
+    uniq = [np.zeros((1, 0), dtype=np.int32)]             # prefixes of each length
+    for d in range(1, depth + 1):
+        codes = _prefix_codes(items[:, :d], V)
+        _, first = np.unique(codes, return_index=True)
+        uniq.append(items[np.sort(first), :d])
+    level_start = np.zeros(depth + 2, dtype=np.int64)
+    for d in range(depth + 1):
+        level_start[d + 1] = level_start[d] + uniq[d].shape[0]
+    n_nodes = int(level_start[depth + 1])
+    child_count = np.zeros(n_nodes, dtype=np.int64)
+    edge_tok, edge_child = [], []
+    for d in range(1, depth + 1):
+        pre = uniq[d]
+        parent_codes = _prefix_codes(pre[:, :d - 1], V)
+        parent_pos = np.searchsorted(_prefix_codes(uniq[d - 1], V), parent_codes) \
+            if d > 1 else np.zeros(pre.shape[0], dtype=np.int64)
+        np.add.at(child_count, level_start[d - 1] + parent_pos, 1)
+        edge_tok.append(pre[:, d - 1])
+        edge_child.append(level_start[d] + np.arange(pre.shape[0]))
+    node_ptr = np.zeros(n_nodes + 1, dtype=np.int64)
+    node_ptr[1:] = np.cumsum(child_count)
+    return SidTrie(items=items, node_ptr=node_ptr.astype(np.int32),
+                   edge_tok=np.concatenate(edge_tok).astype(np.int32),
+                   edge_child=np.concatenate(edge_child).astype(np.int32),
+                   level_start=level_start.astype(np.int32), V=V)
+
+
+@dataclasses.dataclass
+class TrieSelectInputs:
+    """One constrained selection call: a SelectInputs batch whose beams each
+    hold a semantic-ID prefix of `step` tokens taken from the catalog, the
+    trie node of that prefix, and the trie."""
+
+    sel: SelectInputs
+    trie: SidTrie
+    sid: np.ndarray        # [R_old][step] i32, each beam's prefix tokens
+    node_old: np.ndarray   # [R_old] i32, trie node of the prefix (-1: none)
+    step: int
+
+
+def trie_select_inputs(W_old: Sequence[int], W_new: Sequence[int], V: int, step: int,
+                       trie: SidTrie, seed: int, dead: float = 0.0,
+                       logit_std: float = 2.0, score_spread: float = 3.0) -> TrieSelectInputs:
+    """Beams whose prefixes are the first `step` tokens of random catalog
+    items (a fraction `dead` get a prefix no item has, node -1); scores and
+    logits as select_inputs."""
+    sel = select_inputs(W_old, W_new, V, seed, logit_std=logit_std, score_spread=score_spread)
+    rng = np.random.default_rng(seed + 7919)
+    R = int(sel.row_offset_old[-1])
+    pick = rng.integers(0, trie.items.shape[0], size=R)
+    sid = trie.items[pick, :step].astype(np.int32).reshape(R, step)
+    node = trie.node_of(sid) if R else np.zeros(0, np.int32)
+    if dead > 0 and step > 0 and R:
+        kill = rng.random(R) < dead
+        for r in np.nonzero(kill)[0]:
+            for _ in range(64):
+                cand = rng.integers(0, V, size=step).astype(np.int32)
+                if trie.node_of(cand[None, :])[0] < 0:
+                    sid[r] = cand
+                    node[r] = -1
+                    break
+    return TrieSelectInputs(sel=sel, trie=trie, sid=sid, node_old=node.astype(np.int32), step=step)
+
+
+# Constrained selection at the 900-beam shape: a synthetic catalog of one
+# million 3-token items over the 8192-token vocabulary; the benchmarked call
+# is the second step (each beam holds one token; ~120 legal next tokens).
+TRIE_CATALOG = dict(n_items=1_000_000, depth=3, V=8192, seed=9001)
+TRIE_WORKLOADS = {
+    4: dict(name="w900_b4_v8192_items1m_step1", W_old=(900,) * 4, W_new=(900,) * 4, step=1,
+            seed=4507),
+}
+
+_trie_cache: Dict[tuple, SidTrie] = {}
+
+
+def catalog_trie(n_items: int, depth: int, V: int, seed: int) -> SidTrie:
+    key = (n_items, depth, V, seed)
+    if key not in _trie_cache:
+        _trie_cache[key] = build_trie(sid_catalog(n_items, depth, V, seed), V)
+    return _trie_cache[key]
+
+
+def trie_workload(cfg: int) -> TrieSelectInputs:
+    w = dict(TRIE_WORKLOADS[cfg])
+    w.pop("name")
+    trie = catalog_trie(**TRIE_CATALOG)
+    return trie_select_inputs(trie=trie, V=TRIE_CATALOG["V"], **w)
