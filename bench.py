@@ -216,6 +216,7 @@ def write_profile_summaries(d: str):
                   open(os.path.join(out_dir, f"traffic_{name}.json"), "w"), indent=1)
         print(f"wrote profiles/{name}.txt", flush=True)
     write_step_profile(d, f_fetch, f_write, copy_fetch_kib, copy_write_kib)
+    write_select_profile(d, f_fetch, f_write)
 
 
 def write_step_profile(d, f_fetch, f_write, copy_fetch_kib, copy_write_kib):
@@ -260,6 +261,58 @@ def write_step_profile(d, f_fetch, f_write, copy_fetch_kib, copy_write_kib):
     json.dump({"kernel": "beam_step", "workload": name_wl, "kernel_sha": sha,
                "bytes_per_launch": traffic, "fetch_kib": fetch_kib, "write_kib": write_kib,
                "fetch_factor": f_fetch, "write_factor": f_write, "avg_launch_us": avg_us},
+              open(os.path.join(out_dir, f"traffic_{name}.json"), "w"), indent=1)
+    print(f"wrote profiles/{name}.txt", flush=True)
+
+
+def write_select_profile(d, f_fetch, f_write):
+    """Summary of the two beam-selection kernels (profiled with --only select):
+    per-kernel averages and counters, summed per call."""
+    if not os.path.isdir(os.path.join(d, "trace_select")):
+        return
+    si = I.select_workload(SELECT_CFGS[0])
+    name_wl = I.SELECT_WORKLOADS[SELECT_CFGS[0]]["name"]
+    nbytes = algorithmic_select(si)
+    stats = _csv_rows(os.path.join(d, "trace_select"), "kernel_stats.csv")
+    sha = kernel_hash(SELECT_SOURCES)
+    lines = [f"# beam selection (select_rows + select_request) on {name_wl}", "",
+             "kernel trace (rocprofv3 --kernel-trace --stats), command from the repository root:",
+             "    " + PROFILE_COMMANDS["trace"].format(d="gpurun_out/prof", w="select"), "",
+             f"{'kernel':60s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
+    for r in stats:
+        lines.append(f"{r['Name'][:60]:60s} {int(r['Calls']):6d} "
+                     f"{float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
+                     f"{float(r['MaxNs']) / 1e3:9.2f}")
+    lines += ["", "HBM counters, one pass each:",
+              "    " + PROFILE_COMMANDS["fetch"].format(d="gpurun_out/prof", w="select"),
+              "    " + PROFILE_COMMANDS["write"].format(d="gpurun_out/prof", w="select"),
+              "    (copy calibration as in the attention summaries)", ""]
+    avg_us = 0.0
+    traffic = 0.0
+    per = {}
+    for k in SELECT_KERNELS:
+        kern = [r for r in stats if k in r["Name"]]
+        us = float(kern[0]["AverageNs"]) / 1e3 if kern else float("nan")
+        fk, n_f = _counter_per_dispatch(os.path.join(d, "fetch_select"), k, "FETCH_SIZE")
+        wk, n_w = _counter_per_dispatch(os.path.join(d, "write_select"), k, "WRITE_SIZE")
+        t = fk * 1024 * f_fetch + wk * 1024 * f_write
+        per[k] = {"avg_launch_us": us, "fetch_kib": fk, "write_kib": wk, "bytes_per_launch": t}
+        avg_us += us
+        traffic += t
+        lines.append(f"{k:16s} avg {us:9.2f} us  FETCH_SIZE {fk:10.1f} KiB  WRITE_SIZE "
+                     f"{wk:10.1f} KiB  (means of {n_f}, {n_w})  -> {t / 1e6:8.3f} MB")
+    lines += [f"copy factors              fetch {f_fetch:.3f}, write {f_write:.3f}",
+              f"HBM traffic per call      {traffic / 1e6:12.3f} MB",
+              f"algorithmic bytes         {nbytes / 1e6:12.3f} MB  "
+              f"(traffic / algorithmic = {traffic / nbytes:.3f})",
+              f"both kernels, per call    {avg_us:12.2f} us -> {nbytes / avg_us / 1e3:.1f} GB/s",
+              f"kernel sources sha256[:16] {sha}"]
+    name = f"beam_select_{name_wl}"
+    out_dir = os.path.join(ROOT, "profiles")
+    open(os.path.join(out_dir, name + ".txt"), "w").write("\n".join(lines) + "\n")
+    json.dump({"kernel": "beam_select", "workload": name_wl, "kernel_sha": sha,
+               "bytes_per_launch": traffic, "per_kernel": per, "fetch_factor": f_fetch,
+               "write_factor": f_write, "avg_launch_us": avg_us},
               open(os.path.join(out_dir, f"traffic_{name}.json"), "w"), indent=1)
     print(f"wrote profiles/{name}.txt", flush=True)
 
