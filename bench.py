@@ -46,6 +46,7 @@ STEP_CFGS = (4, 2)            # beam-step shapes reported (900 and 128 beams)
 SELECT_SOURCES = ["shared_prefix_beam_amd/csrc/gr_beam_select.hip"]
 SELECT_CFGS = (4, 2)          # beam-selection shapes reported (900 and 128 beams)
 SELECT_KERNELS = ("select_rows", "select_request")
+TRIE_CFGS = (4,)              # constrained-selection shape reported (900 beams, second step)
 PAGE_SIZE = 16                # tokens per page of the paged-ContextKV measurement
 
 
@@ -94,6 +95,22 @@ def algorithmic_select(si: I.SelectInputs) -> int:
     B = si.row_offset_old.size - 1
     R_new = int(si.row_offset_new[-1])
     return 4 * R_old * V + 4 * R_old + 8 * (B + 1) + 12 * R_new
+
+
+def algorithmic_trie(ti: I.TrieSelectInputs) -> int:
+    """Bytes one constrained selection must move, each once: per beam its
+    node id, the node's two CSR offsets and its score; per legal edge its
+    label and the logit it selects; the row offsets; and per kept beam the
+    score, parent, token and node written, with the chosen edge's label and
+    child read."""
+    si, tr = ti.sel, ti.trie
+    fan = np.diff(tr.node_ptr)
+    live = ti.node_old >= 0
+    n_edges = int(fan[ti.node_old[live]].sum())
+    R_old = si.logits.shape[0]
+    B = si.row_offset_old.size - 1
+    R_new = int(si.row_offset_new[-1])
+    return 4 * R_old + 4 * R_old + 8 * int(live.sum()) + 8 * n_edges + 8 * (B + 1) + 24 * R_new
 
 
 def kernel_hash(sources=None) -> str:
@@ -171,6 +188,8 @@ def write_profile_summaries(d: str):
     f_write, copy_write_kib = _copy_factor(os.path.join(d, "copy_write"), "WRITE_SIZE")
     sha = kernel_hash()
     for which, cfg in (("primary", PRIMARY), ("secondary", SECONDARY)):
+        if not os.path.isdir(os.path.join(d, f"trace_{which}")):
+            continue                                # not profiled in this folder
         wl = I.WORKLOADS[cfg]
         stats = [r for r in _csv_rows(os.path.join(d, f"trace_{which}"), "kernel_stats.csv")]
         fetch_kib, n_f = _counter_per_dispatch(os.path.join(d, f"fetch_{which}"),
@@ -217,6 +236,7 @@ def write_profile_summaries(d: str):
         print(f"wrote profiles/{name}.txt", flush=True)
     write_step_profile(d, f_fetch, f_write, copy_fetch_kib, copy_write_kib)
     write_select_profile(d, f_fetch, f_write)
+    write_select_profile(d, f_fetch, f_write, w="trie")
 
 
 def write_step_profile(d, f_fetch, f_write, copy_fetch_kib, copy_write_kib):
@@ -265,27 +285,34 @@ def write_step_profile(d, f_fetch, f_write, copy_fetch_kib, copy_write_kib):
     print(f"wrote profiles/{name}.txt", flush=True)
 
 
-def write_select_profile(d, f_fetch, f_write):
-    """Summary of the two beam-selection kernels (profiled with --only select):
-    per-kernel averages and counters, summed per call."""
-    if not os.path.isdir(os.path.join(d, "trace_select")):
+def write_select_profile(d, f_fetch, f_write, w="select"):
+    """Summary of the two beam-selection kernels (profiled with --only select,
+    or --only trie for the constrained call): per-kernel averages and
+    counters, summed per call."""
+    if not os.path.isdir(os.path.join(d, f"trace_{w}")):
         return
-    si = I.select_workload(SELECT_CFGS[0])
-    name_wl = I.SELECT_WORKLOADS[SELECT_CFGS[0]]["name"]
-    nbytes = algorithmic_select(si)
-    stats = _csv_rows(os.path.join(d, "trace_select"), "kernel_stats.csv")
+    if w == "trie":
+        ti = I.trie_workload(TRIE_CFGS[0])
+        name_wl = I.TRIE_WORKLOADS[TRIE_CFGS[0]]["name"]
+        nbytes = algorithmic_trie(ti)
+        title, kname = "constrained beam selection", "beam_select_trie"
+    else:
+        name_wl = I.SELECT_WORKLOADS[SELECT_CFGS[0]]["name"]
+        nbytes = algorithmic_select(I.select_workload(SELECT_CFGS[0]))
+        title, kname = "beam selection", "beam_select"
+    stats = _csv_rows(os.path.join(d, f"trace_{w}"), "kernel_stats.csv")
     sha = kernel_hash(SELECT_SOURCES)
-    lines = [f"# beam selection (select_rows + select_request) on {name_wl}", "",
+    lines = [f"# {title} (select_rows + select_request) on {name_wl}", "",
              "kernel trace (rocprofv3 --kernel-trace --stats), command from the repository root:",
-             "    " + PROFILE_COMMANDS["trace"].format(d="gpurun_out/prof", w="select"), "",
+             "    " + PROFILE_COMMANDS["trace"].format(d="gpurun_out/prof", w=w), "",
              f"{'kernel':60s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
     for r in stats:
         lines.append(f"{r['Name'][:60]:60s} {int(r['Calls']):6d} "
                      f"{float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
                      f"{float(r['MaxNs']) / 1e3:9.2f}")
     lines += ["", "HBM counters, one pass each:",
-              "    " + PROFILE_COMMANDS["fetch"].format(d="gpurun_out/prof", w="select"),
-              "    " + PROFILE_COMMANDS["write"].format(d="gpurun_out/prof", w="select"),
+              "    " + PROFILE_COMMANDS["fetch"].format(d="gpurun_out/prof", w=w),
+              "    " + PROFILE_COMMANDS["write"].format(d="gpurun_out/prof", w=w),
               "    (copy calibration as in the attention summaries)", ""]
     avg_us = 0.0
     traffic = 0.0
@@ -293,8 +320,8 @@ def write_select_profile(d, f_fetch, f_write):
     for k in SELECT_KERNELS:
         kern = [r for r in stats if k in r["Name"]]
         us = float(kern[0]["AverageNs"]) / 1e3 if kern else float("nan")
-        fk, n_f = _counter_per_dispatch(os.path.join(d, "fetch_select"), k, "FETCH_SIZE")
-        wk, n_w = _counter_per_dispatch(os.path.join(d, "write_select"), k, "WRITE_SIZE")
+        fk, n_f = _counter_per_dispatch(os.path.join(d, f"fetch_{w}"), k, "FETCH_SIZE")
+        wk, n_w = _counter_per_dispatch(os.path.join(d, f"write_{w}"), k, "WRITE_SIZE")
         t = fk * 1024 * f_fetch + wk * 1024 * f_write
         per[k] = {"avg_launch_us": us, "fetch_kib": fk, "write_kib": wk, "bytes_per_launch": t}
         avg_us += us
@@ -307,10 +334,10 @@ def write_select_profile(d, f_fetch, f_write):
               f"(traffic / algorithmic = {traffic / nbytes:.3f})",
               f"both kernels, per call    {avg_us:12.2f} us -> {nbytes / avg_us / 1e3:.1f} GB/s",
               f"kernel sources sha256[:16] {sha}"]
-    name = f"beam_select_{name_wl}"
+    name = f"{kname}_{name_wl}"
     out_dir = os.path.join(ROOT, "profiles")
     open(os.path.join(out_dir, name + ".txt"), "w").write("\n".join(lines) + "\n")
-    json.dump({"kernel": "beam_select", "workload": name_wl, "kernel_sha": sha,
+    json.dump({"kernel": kname, "workload": name_wl, "kernel_sha": sha,
                "bytes_per_launch": traffic, "per_kernel": per, "fetch_factor": f_fetch,
                "write_factor": f_write, "avg_launch_us": avg_us},
               open(os.path.join(out_dir, f"traffic_{name}.json"), "w"), indent=1)
@@ -479,14 +506,16 @@ def measure_step(cfg: int, steps: int, warmup: int):
                 n_sets=n_sets, bit_exact=bool(ok))
 
 
-def measure_select(cfg: int, steps: int, warmup: int):
-    """Time gr_beam_select on the selection workload `cfg` (both launches of
-    one call between one event pair), rotating input sets like `measure`."""
+def measure_select(cfg: int, steps: int, warmup: int, trie: bool = False):
+    """Time gr_beam_select (gr_beam_select_trie with `trie`) on the selection
+    workload `cfg` (both launches of one call between one event pair),
+    rotating input sets like `measure`."""
     import torch
     from shared_prefix_beam_amd import gr_attn
 
-    si = I.select_workload(cfg)
-    nbytes = algorithmic_select(si)
+    ti = I.trie_workload(cfg) if trie else None
+    si = ti.sel if trie else I.select_workload(cfg)
+    nbytes = algorithmic_trie(ti) if trie else algorithmic_select(si)
     R_old, V = si.logits.shape
     B = si.row_offset_old.size - 1
     R_new = int(si.row_offset_new[-1])
@@ -496,28 +525,64 @@ def measure_select(cfg: int, steps: int, warmup: int):
                 ro_new=torch.from_numpy(si.row_offset_new).to(dev),
                 score_old=torch.from_numpy(si.score_old).to(dev),
                 logits=torch.from_numpy(np.ascontiguousarray(si.logits)).to(dev))
-    n_sets = max(2, int(np.ceil(2 * MALL_BYTES / nbytes)) + 1)
+    if trie:
+        def i32(a):
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+        base["node_old"] = i32(ti.node_old)
+        t_trie = dict(node_ptr=i32(ti.trie.node_ptr), edge_tok=i32(ti.trie.edge_tok),
+                      edge_child=i32(ti.trie.edge_child))
+        # the largest fanout among this step's nodes (a catalog knows it per
+        # level); it sizes the row launch
+        fan = int(np.diff(ti.trie.node_ptr)[ti.node_old[ti.node_old >= 0]].max())
+    # the logits dominate the bytes the sets occupy; rotate past the MALL
+    set_bytes = 4 * R_old * V
+    n_sets = max(2, int(np.ceil(2 * MALL_BYTES / set_bytes)) + 1)
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(n_sets - 1)]
     score_new = torch.empty(R_new, dtype=torch.float32, device=dev)
     parent = torch.empty(R_new, dtype=torch.int32, device=dev)
     token = torch.empty(R_new, dtype=torch.int32, device=dev)
+    node_new = torch.empty(R_new, dtype=torch.int32, device=dev)
     dims = gr_attn.SelectDims(B=B, R_old=R_old, R_new=R_new, V=V, K_max=K_max, reserved=0)
     ws_bytes = gr_attn.gr_beam_select_workspace_bytes(dims)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     for t in sets:   # the front end validates every set once
-        gr_attn.beam_select(t["ro_old"], t["ro_new"], t["score_old"], t["logits"], K_max,
-                            score_new=score_new, parent=parent, token=token, workspace=ws,
-                            stream=stream)
-    order = ("ro_old", "ro_new", "score_old", "logits")
-    args = [tuple(t[k].data_ptr() for k in order) for t in sets]
-    outs = (score_new.data_ptr(), parent.data_ptr(), token.data_ptr(), ws.data_ptr(), ws_bytes)
+        if trie:
+            gr_attn.beam_select_trie(t["ro_old"], t["ro_new"], t["score_old"], t["logits"],
+                                     t["node_old"], t_trie["node_ptr"], t_trie["edge_tok"],
+                                     t_trie["edge_child"], K_max, fan, score_new=score_new,
+                                     parent=parent, token=token, node_new=node_new,
+                                     workspace=ws, stream=stream)
+        else:
+            gr_attn.beam_select(t["ro_old"], t["ro_new"], t["score_old"], t["logits"], K_max,
+                                score_new=score_new, parent=parent, token=token, workspace=ws,
+                                stream=stream)
     handle = stream.cuda_stream
+    if trie:
+        desc = gr_attn.SidTrie(node_ptr=t_trie["node_ptr"].data_ptr(),
+                               edge_tok=t_trie["edge_tok"].data_ptr(),
+                               edge_child=t_trie["edge_child"].data_ptr(),
+                               n_nodes=ti.trie.n_nodes, n_edges=ti.trie.n_edges,
+                               max_fanout=fan, reserved=0)
+        args = [tuple(t[k].data_ptr() for k in ("ro_old", "ro_new", "score_old", "logits",
+                                                 "node_old")) for t in sets]
+        outs = (score_new.data_ptr(), parent.data_ptr(), token.data_ptr(), node_new.data_ptr(),
+                ws.data_ptr(), ws_bytes)
 
-    def call(i):
-        rc = gr_attn.gr_beam_select(dims, *args[i % n_sets], *outs, handle)
-        if rc != gr_attn.GR_OK:
-            raise gr_attn.GrAttnError(rc, "gr_beam_select")
+        def call(i):
+            rc = gr_attn.gr_beam_select_trie(dims, desc, *args[i % n_sets], *outs, handle)
+            if rc != gr_attn.GR_OK:
+                raise gr_attn.GrAttnError(rc, "gr_beam_select_trie")
+    else:
+        args = [tuple(t[k].data_ptr() for k in ("ro_old", "ro_new", "score_old", "logits"))
+                for t in sets]
+        outs = (score_new.data_ptr(), parent.data_ptr(), token.data_ptr(), ws.data_ptr(),
+                ws_bytes)
+
+        def call(i):
+            rc = gr_attn.gr_beam_select(dims, *args[i % n_sets], *outs, handle)
+            if rc != gr_attn.GR_OK:
+                raise gr_attn.GrAttnError(rc, "gr_beam_select")
 
     for i in range(warmup):
         call(i)
@@ -533,23 +598,33 @@ def measure_select(cfg: int, steps: int, warmup: int):
     # spot check against the oracle (not timed): the last call used set
     # (steps - 1) % n_sets, identical to the first
     from oracle import oracle as O
-    o_s, o_p, o_t = O.beam_select(si.row_offset_old, si.row_offset_new, si.score_old, si.logits)
+    if trie:
+        o_s, o_p, o_t, o_n = O.beam_select_trie(
+            si.row_offset_old, si.row_offset_new, si.score_old, si.logits, ti.sid,
+            ti.trie.node_ptr, ti.trie.edge_tok, ti.trie.edge_child)
+    else:
+        o_s, o_p, o_t = O.beam_select(si.row_offset_old, si.row_offset_new, si.score_old,
+                                      si.logits)
     g_s, g_p, g_t = (x.cpu().numpy() for x in (score_new, parent, token))
     same = (g_p == o_p) & (g_t == o_t)
+    if trie:
+        same &= node_new.cpu().numpy() == o_n
     err = float(np.abs(g_s[same].astype(np.float64) - o_s[same]).max()) if same.any() else None
-    return dict(si=si, name=I.SELECT_WORKLOADS[cfg]["name"], nbytes=nbytes, launch_ms=launch_ms,
+    name = (I.TRIE_WORKLOADS if trie else I.SELECT_WORKLOADS)[cfg]["name"]
+    return dict(si=si, name=name, nbytes=nbytes, launch_ms=launch_ms, trie=trie,
                 n_sets=n_sets, R_new=R_new, rank_match=float(same.mean()), max_abs=err)
 
 
 def select_entry(r) -> dict:
     gbs = r["nbytes"] / (r["launch_ms"] * 1e-3) / 1e9
+    kern = "beam_select_trie" if r["trie"] else "beam_select"
     return {"workload": r["name"], "rows_in": int(r["si"].logits.shape[0]),
             "beams_kept": r["R_new"], "launch_us": r["launch_ms"] * 1e3,
             "value": r["R_new"] / (r["launch_ms"] * 1e-3), "unit": "beams-selected/s",
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": gbs / PEAK_HBM_GBS,
-                         "traffic": recorded_traffic(r["name"], "beam_select", SELECT_SOURCES),
-                         "kernel": "beam_select (select_rows + select_request)",
+                         "traffic": recorded_traffic(r["name"], kern, SELECT_SOURCES),
+                         "kernel": kern + " (select_rows + select_request)",
                          "algorithmic_bytes": r["nbytes"]},
             "input_copies_rotated": r["n_sets"],
             "spot_check": {"rank_match": r["rank_match"], "max_abs": r["max_abs"]}}
@@ -592,7 +667,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--only", choices=["primary", "secondary", "beam_step", "select"],
+    ap.add_argument("--only", choices=["primary", "secondary", "beam_step", "select", "trie"],
                     help="time one workload only and print its launch time (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run 10 device copies of 256 MiB (reference for HBM byte counters)")
@@ -621,8 +696,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": 256 << 20, "launches": 10}), flush=True)
         return
-    if args.only == "select":
-        r = measure_select(SELECT_CFGS[0], args.steps, args.warmup)
+    if args.only in ("select", "trie"):
+        r = (measure_select(TRIE_CFGS[0], args.steps, args.warmup, trie=True)
+             if args.only == "trie" else measure_select(SELECT_CFGS[0], args.steps, args.warmup))
         print(json.dumps({"workload": r["name"], "launch_us": r["launch_ms"] * 1e3,
                           "rank_match": r["rank_match"]}), flush=True)
         return
@@ -682,6 +758,8 @@ def main():
     line["beam_step"] = [step_entry(measure_step(c, args.steps, args.warmup)) for c in STEP_CFGS]
     line["beam_select"] = [select_entry(measure_select(c, args.steps, args.warmup))
                            for c in SELECT_CFGS]
+    line["beam_select_trie"] = [select_entry(measure_select(c, args.steps, args.warmup, trie=True))
+                                for c in TRIE_CFGS]
     paged = []
     for cfg, dense in ((PRIMARY, prim), (SECONDARY, sec)):
         if dense is None:

@@ -255,6 +255,53 @@ int gr_beam_select(const gr_beam_select_dims *dims, const int32_t *row_offset_ol
                    float *score_new, int32_t *parent, int32_t *token, void *workspace,
                    size_t workspace_bytes, void *stream);
 
+/*
+ * Item catalog as a prefix trie of semantic-ID tokens in CSR form, resident
+ * in device memory (GR-Inference blog, kernel design: the SID trie stored as
+ * CSR).  Node 0 is the root.  Node u's children are edges node_ptr[u] ..
+ * node_ptr[u+1]-1; edge e carries token edge_tok[e] (in [0, V), strictly
+ * increasing within a node) and leads to node edge_child[e].  max_fanout
+ * bounds every node's child count (1 .. V): it sizes the launch, and a node
+ * with more children has only its first max_fanout considered.
+ */
+typedef struct gr_sid_trie {
+    const int32_t *node_ptr;   /* DEVICE int32 [n_nodes + 1] */
+    const int32_t *edge_tok;   /* DEVICE int32 [n_edges] */
+    const int32_t *edge_child; /* DEVICE int32 [n_edges] */
+    int32_t n_nodes;           /* >= 1 */
+    int32_t n_edges;           /* >= 0 */
+    int32_t max_fanout;        /* 1 .. V */
+    int32_t reserved;          /* must be 0 */
+} gr_sid_trie;
+
+/*
+ * Item-constrained beam selection: gr_beam_select where beam w's candidates
+ * are only the legal next tokens, the labels of the edges leaving its trie
+ * node node_old[w] (none if node_old[w] is -1 or out of range).  The prefix
+ * traversal, the gather of the legal logits and the top-K run in one call
+ * (GR-Inference blog, kernel design: item-constrained fused kernel; xGR
+ * review, section "xBeam").  A legal candidate (w, t) is valued
+ *     score_old[w] + logits[w][t] - ln sum_{legal u} exp(logits[w][u])
+ * (log_softmax over the legal tokens: every other logit masked to -inf),
+ * ranked and packed as in gr_beam_select.  node_new[k] is the trie node of
+ * the kept beam's prefix extended by its token (the child on that edge),
+ * -1 for padding: the next step's node_old.  Only the legal logits of a row
+ * are read.
+ *
+ * Layouts as gr_beam_select, plus node_old int32 [R_old] and node_new int32
+ * [R_new] (DEVICE); trie is host memory holding device pointers.  The same
+ * workspace size applies.  Errors as gr_beam_select; a NULL or inconsistent
+ * trie (n_nodes < 1, n_edges < 0, max_fanout outside 1 .. V, reserved != 0)
+ * gives GR_ERR_NULL or GR_ERR_DIMS.  Trie contents are read as given:
+ * out-of-range node or edge ranges are clamped (wrong results, no access
+ * outside the arrays); labels outside [0, V) count as -inf logits.
+ */
+int gr_beam_select_trie(const gr_beam_select_dims *dims, const gr_sid_trie *trie,
+                        const int32_t *row_offset_old, const int32_t *row_offset_new,
+                        const float *score_old, const float *logits, const int32_t *node_old,
+                        float *score_new, int32_t *parent, int32_t *token, int32_t *node_new,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *gr_status_str(int status);
 

@@ -371,10 +371,12 @@ size_t gr_beam_select_workspace_bytes(const gr_beam_select_dims *d)
     return gr::beam_select_workspace(d->R_old, d->K_max);
 }
 
-int gr_beam_select(const gr_beam_select_dims *d, const int32_t *row_offset_old,
-                   const int32_t *row_offset_new, const float *score_old, const float *logits,
-                   float *score_new, int32_t *parent, int32_t *token, void *workspace,
-                   size_t workspace_bytes, void *stream)
+static int beam_select_common(const gr_beam_select_dims *d, const gr_sid_trie *trie,
+                              const int32_t *row_offset_old, const int32_t *row_offset_new,
+                              const float *score_old, const float *logits,
+                              const int32_t *node_old, float *score_new, int32_t *parent,
+                              int32_t *token, int32_t *node_new, void *workspace,
+                              size_t workspace_bytes, void *stream)
 {
     if (!d)
         return GR_ERR_NULL;
@@ -384,6 +386,15 @@ int gr_beam_select(const gr_beam_select_dims *d, const int32_t *row_offset_old,
     if (d->V > gr::SEL_MAX_V || d->K_max > gr::SEL_MAX_K ||
         static_cast<int64_t>(d->R_old) * d->V > INT32_MAX)
         return GR_ERR_UNSUPPORTED;
+    if (trie) {
+        if (trie->n_nodes < 1 || trie->n_edges < 0 || trie->max_fanout < 1 ||
+            trie->max_fanout > d->V || trie->reserved != 0)
+            return GR_ERR_DIMS;
+        if (!trie->node_ptr || (trie->n_edges > 0 && (!trie->edge_tok || !trie->edge_child)))
+            return GR_ERR_NULL;
+        if ((d->R_old > 0 && !node_old) || (d->R_new > 0 && !node_new))
+            return GR_ERR_NULL;
+    }
     if (d->B > 0 && (!row_offset_old || !row_offset_new))
         return GR_ERR_NULL;
     if (d->R_old > 0 && (!score_old || !logits))
@@ -396,7 +407,9 @@ int gr_beam_select(const gr_beam_select_dims *d, const int32_t *row_offset_old,
     if (workspace_bytes < need)
         return GR_ERR_DIMS;
     const void *al4[] = {row_offset_old, row_offset_new, score_old, logits, score_new, parent,
-                         token};
+                         token, node_old, node_new,
+                         trie ? trie->node_ptr : nullptr, trie ? trie->edge_tok : nullptr,
+                         trie ? trie->edge_child : nullptr};
     for (const void *p : al4)
         if (p && (reinterpret_cast<uintptr_t>(p) & 3u))
             return GR_ERR_ALIGN;
@@ -426,6 +439,20 @@ int gr_beam_select(const gr_beam_select_dims *d, const int32_t *row_offset_old,
         p.ws_ovf = reinterpret_cast<int32_t *>(w);
         w += al(R * sizeof(int32_t));
         p.ws_surv = reinterpret_cast<uint64_t *>(w);
+        w += al(R * static_cast<size_t>(d->K_max) * sizeof(uint64_t));
+        p.ws_n = reinterpret_cast<int32_t *>(w);
+        w += al(R * sizeof(int32_t));
+        p.ws_e0 = reinterpret_cast<int32_t *>(w);
+    }
+    if (trie) {
+        p.node_ptr = trie->node_ptr;
+        p.edge_tok = trie->edge_tok;
+        p.edge_child = trie->edge_child;
+        p.n_nodes = trie->n_nodes;
+        p.n_edges = trie->n_edges;
+        p.max_fanout = trie->max_fanout;
+        p.node_old = node_old;
+        p.node_new = node_new;
     }
     p.B = d->B;
     p.R_old = d->R_old;
@@ -434,6 +461,29 @@ int gr_beam_select(const gr_beam_select_dims *d, const int32_t *row_offset_old,
     p.K_max = d->K_max;
     const hipError_t e = gr::launch_beam_select(p, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GR_OK : GR_ERR_LAUNCH;
+}
+
+int gr_beam_select(const gr_beam_select_dims *d, const int32_t *row_offset_old,
+                   const int32_t *row_offset_new, const float *score_old, const float *logits,
+                   float *score_new, int32_t *parent, int32_t *token, void *workspace,
+                   size_t workspace_bytes, void *stream)
+{
+    return beam_select_common(d, nullptr, row_offset_old, row_offset_new, score_old, logits,
+                              nullptr, score_new, parent, token, nullptr, workspace,
+                              workspace_bytes, stream);
+}
+
+int gr_beam_select_trie(const gr_beam_select_dims *d, const gr_sid_trie *trie,
+                        const int32_t *row_offset_old, const int32_t *row_offset_new,
+                        const float *score_old, const float *logits, const int32_t *node_old,
+                        float *score_new, int32_t *parent, int32_t *token, int32_t *node_new,
+                        void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!trie)
+        return GR_ERR_NULL;
+    return beam_select_common(d, trie, row_offset_old, row_offset_new, score_old, logits,
+                              node_old, score_new, parent, token, node_new, workspace,
+                              workspace_bytes, stream);
 }
 
 const char *gr_status_str(int status)

@@ -54,9 +54,16 @@ struct SelParams {
     float *ws_off;       // [R_old] score_old - LSE of each row
     int32_t *ws_ovf;     // [R_old] rows to select again, per request from row_offset_old[b]
     uint64_t *ws_surv;   // [R_old][K_max] survivors, per request from row_offset_old[b]*K_max
+    int32_t *ws_n;       // [R_old] candidates of each row (V when unconstrained)
+    int32_t *ws_e0;      // [R_old] first trie edge of each row's node
+    // item-constrained selection (node_ptr == nullptr: every token is legal)
+    const int32_t *node_ptr, *edge_tok, *edge_child;
+    const int32_t *node_old;   // [R_old] trie node of each beam (-1: none)
+    int32_t *node_new;         // [R_new]
+    int n_nodes, n_edges, max_fanout;
     int B, R_old, R_new, V, K_max;
 };
-// Workspace bytes of the four tables above (each 256-byte aligned).
+// Workspace bytes of the six tables above (each 256-byte aligned).
 size_t beam_select_workspace(int R_old, int K_max);
 
 // Longest key list the generic comparator keeps in LDS.

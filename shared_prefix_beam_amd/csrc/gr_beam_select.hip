@@ -309,8 +309,31 @@ __device__ __forceinline__ int request_of(const int32_t *row_offset, int B, int 
     return lo;
 }
 
-// One beam row per workgroup; NV logits per thread (V <= NV * 256).
-template <int NV>
+// Candidates of a beam row: every token (TRIE false), or the labels of the
+// edges leaving the beam's trie node (TRIE true): candidate v is edge e0 + v,
+// token edge_tok[e0 + v].  A key's index part is w * V + v; the edge labels
+// increase with v, so ties still go to the smaller token.
+__device__ __forceinline__ void row_candidates(const SelParams &p, int r, bool trie, int cap,
+                                               int &n, int &e0)
+{
+    n = p.V;
+    e0 = 0;
+    if (trie) {
+        n = 0;
+        const int node = p.node_old[r];
+        if (node >= 0 && node < p.n_nodes) {
+            int a = p.node_ptr[node], z = p.node_ptr[node + 1];
+            a = a < 0 ? 0 : (a > p.n_edges ? p.n_edges : a);
+            z = z < a ? a : (z > p.n_edges ? p.n_edges : z);
+            e0 = a;
+            n = z - a < p.V ? z - a : p.V;          // distinct labels below V
+            n = n < cap ? n : cap;
+        }
+    }
+}
+
+// One beam row per workgroup; NV candidates per thread (n <= NV * 256).
+template <int NV, bool TRIE>
 __global__ __launch_bounds__(SEL_ROW_THREADS) void select_rows(const SelParams p)
 {
     constexpr int NT = SEL_ROW_THREADS, NW = NT / 64;
@@ -335,13 +358,28 @@ __global__ __launch_bounds__(SEL_ROW_THREADS) void select_rows(const SelParams p
     if (k_row <= 0)
         return;
     const int L = k_row < SEL_LIST ? k_row : SEL_LIST;
+    int n, e0;
+    row_candidates(p, r, TRIE, NV * NT, n, e0);
+    if (tid == 0) {
+        p.ws_n[r] = n;
+        p.ws_e0[r] = e0;
+    }
+    uint64_t *list = p.ws_list + (int64_t)r * SEL_LIST;
+    if (n == 0) {                                 // no legal token: an empty list
+        if (tid < L)
+            list[tid] = 0;
+        return;
+    }
 
     const float *row = p.logits + (int64_t)r * p.V;
     float x[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int v = tid + NT * i;
-        x[i] = v < p.V ? row[v] : -__builtin_huge_valf();
+        int t = v;
+        if (TRIE && v < n)
+            t = p.edge_tok[e0 + v];
+        x[i] = (v < n && t >= 0 && t < p.V) ? row[t] : -__builtin_huge_valf();
     }
     // max and log-sum-exp over the row
     float m = x[0];
@@ -378,12 +416,12 @@ __global__ __launch_bounds__(SEL_ROW_THREADS) void select_rows(const SelParams p
     // the candidates' ordered value bits replace the logits
     uint32_t o[NV];
     const uint32_t flat0 = (uint32_t)wl * (uint32_t)p.V + (uint32_t)tid;
-    const bool has = tid < p.V;
+    const bool has = tid < n;
     uint64_t tmax = 0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         o[i] = ord_f32(off_w + x[i]);
-        if (tid + NT * i < p.V) {
+        if (tid + NT * i < n) {
             const uint64_t key = make_key(o[i], flat0 + NT * i);
             tmax = key > tmax ? key : tmax;
         }
@@ -393,7 +431,7 @@ __global__ __launch_bounds__(SEL_ROW_THREADS) void select_rows(const SelParams p
     // bounds q distinct keys of the wave from below, and the smallest of the
     // NW bounds L distinct keys; otherwise t0 = 0 (fewer than NT keys)
     uint64_t t0 = 0;
-    if (p.V >= NT) {
+    if (n >= NT) {
         const int q = (L + NW - 1) / NW;
         uint64_t res = 0;
         for (int bit = 63; bit >= 0; --bit) {
@@ -413,7 +451,7 @@ __global__ __launch_bounds__(SEL_ROW_THREADS) void select_rows(const SelParams p
     int c = 0;
 #pragma unroll
     for (int i = 0; i < NV; ++i)
-        c += (tid + NT * i < p.V && make_key(o[i], flat0 + NT * i) >= t0) ? 1 : 0;
+        c += (tid + NT * i < n && make_key(o[i], flat0 + NT * i) >= t0) ? 1 : 0;
     int M;
     const int incl = block_incl_scan<NT>(c, wsum, M);
     if (M <= SEL_CAND) {
@@ -421,7 +459,7 @@ __global__ __launch_bounds__(SEL_ROW_THREADS) void select_rows(const SelParams p
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const uint64_t key = make_key(o[i], flat0 + NT * i);
-            if (tid + NT * i < p.V && key >= t0)
+            if (tid + NT * i < n && key >= t0)
                 cand[at++] = key;
         }
         __syncthreads();
@@ -432,8 +470,10 @@ __global__ __launch_bounds__(SEL_ROW_THREADS) void select_rows(const SelParams p
             for (int j = 0; j < M; ++j)
                 rk += cand[j] > mine ? 1 : 0;
             if (rk < L)
-                p.ws_list[(int64_t)r * SEL_LIST + rk] = mine;
+                list[rk] = mine;
         }
+        if (tid >= M && tid < L)                  // fewer candidates than L: pad
+            list[tid] = 0;
         return;
     }
     // many keys at or above t0: radix select of the L best among them
@@ -448,7 +488,7 @@ __global__ __launch_bounds__(SEL_ROW_THREADS) void select_rows(const SelParams p
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
                 const uint64_t key = make_key(o[i], flat0 + NT * i);
-                if (tid + NT * i < p.V && key >= t0)
+                if (tid + NT * i < n && key >= t0)
                     f(key);
             }
         },
@@ -459,7 +499,7 @@ __global__ __launch_bounds__(SEL_ROW_THREADS) void select_rows(const SelParams p
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const uint64_t key = make_key(o[i], flat0 + NT * i);
-        const bool take = tid + NT * i < p.V && key >= t0 && (key & mk) >= pf;
+        const bool take = tid + NT * i < n && key >= t0 && (key & mk) >= pf;
         const int at = wave_append(take, &n_buf);
         if (take && at < L)
             buf[at] = key;
@@ -470,7 +510,7 @@ __global__ __launch_bounds__(SEL_ROW_THREADS) void select_rows(const SelParams p
         int rk = 0;
         for (int j = 0; j < L; ++j)
             rk += buf[j] > mine ? 1 : 0;
-        p.ws_list[(int64_t)r * SEL_LIST + rk] = mine;
+        list[rk] = mine;
     }
 }
 
@@ -585,6 +625,7 @@ __global__ __launch_bounds__(SEL_REQ_THREADS) void select_request(const SelParam
         radix_kth<NT>(K_eff, kmax, kmin, visit, hist3, hb, pf, mk);
         tau = pf;                                   // the K_eff selected keys are >= pf
     }
+    tau = tau > 1 ? tau : 1;                        // every real key is >= 1; 0 pads
 
     // 2. Survivors: each row's list entries >= tau (a prefix: the lists are
     //    sorted); a row's count is the popcount of its lanes in two ballots.
@@ -605,7 +646,8 @@ __global__ __launch_bounds__(SEL_REQ_THREADS) void select_request(const SelParam
             const uint64_t gm = (1ull << (SEL_LIST / 2)) - 1ull;
             const int c = __popcll((ba >> sh) & gm) + __popcll((bb >> sh) & gm);
             if (kp == 0 && in) {
-                const bool ovf = c == L && L < k_row;
+                // the whole list clears tau and the row has more candidates
+                const bool ovf = c == L && L < k_row && p.ws_n[r0 + base + rl] > L;
                 cnt_lds[rl] = ovf ? 0 : c;
                 if (ovf)
                     ovf_rows[atomicAdd(&n_ovf, 1)] = base + rl;
@@ -649,6 +691,8 @@ __global__ __launch_bounds__(SEL_REQ_THREADS) void select_request(const SelParam
         const int r = r0 + w;
         const float off_w = p.ws_off[r];
         const float *row = p.logits + (int64_t)r * p.V;
+        const int n = p.ws_n[r], e0 = p.ws_e0[r];
+        const bool trie = p.node_ptr != nullptr;
         const uint32_t flat0 = (uint32_t)w * (uint32_t)p.V + (uint32_t)tid;
         uint32_t o[SEL_REQ_NV];
         uint64_t kmax = 0, kmin = ~0ull;
@@ -656,9 +700,13 @@ __global__ __launch_bounds__(SEL_REQ_THREADS) void select_request(const SelParam
 #pragma unroll
         for (int i = 0; i < SEL_REQ_NV; ++i) {
             const int v = tid + NT * i;
-            o[i] = v < p.V ? ord_f32(off_w + row[v]) : 0;
+            int t = v;
+            if (trie && v < n)
+                t = p.edge_tok[e0 + v];
+            const float xv = (v < n && t >= 0 && t < p.V) ? row[t] : -__builtin_huge_valf();
+            o[i] = v < n ? ord_f32(off_w + xv) : 0;
             const uint64_t key = make_key(o[i], flat0 + NT * i);
-            if (v < p.V && key >= tau) {
+            if (v < n && key >= tau) {
                 kmax = key > kmax ? key : kmax;
                 kmin = key < kmin ? key : kmin;
                 ++cnt;
@@ -672,7 +720,7 @@ __global__ __launch_bounds__(SEL_REQ_THREADS) void select_request(const SelParam
 #pragma unroll
             for (int i = 0; i < SEL_REQ_NV; ++i) {
                 const uint64_t key = make_key(o[i], flat0 + NT * i);
-                if (tid + NT * i < p.V && key >= tau)
+                if (tid + NT * i < n && key >= tau)
                     f(key);
             }
         };
@@ -683,7 +731,7 @@ __global__ __launch_bounds__(SEL_REQ_THREADS) void select_request(const SelParam
 #pragma unroll
         for (int i = 0; i < SEL_REQ_NV; ++i) {
             const uint64_t key = make_key(o[i], flat0 + NT * i);
-            const bool sel = tid + NT * i < p.V && key >= tau && (key & mk) >= pf;
+            const bool sel = tid + NT * i < n && key >= tau && (key & mk) >= pf;
             const int at = wave_append(sel, &n_sel);
             if (sel && at < take)
                 surv[N + at] = key;
@@ -767,22 +815,34 @@ __global__ __launch_bounds__(SEL_REQ_THREADS) void select_request(const SelParam
     }
     __syncthreads();                                // xch2 is the sort's exchange
     key = block_sort_desc<NT>(key, ns, xch2);
+    const bool trie = p.node_ptr != nullptr;
     if (tid < K) {
         if (tid < take) {
             const uint32_t flat = ~(uint32_t)key;
+            const int w = (int)(flat / (uint32_t)p.V), v = (int)(flat % (uint32_t)p.V);
             p.score_new[k0 + tid] = unord_f32((uint32_t)(key >> 32));
-            p.parent[k0 + tid] = (int)(flat / (uint32_t)p.V);
-            p.token[k0 + tid] = (int)(flat % (uint32_t)p.V);
+            p.parent[k0 + tid] = w;
+            if (trie) {
+                const int e = p.ws_e0[r0 + w] + v;
+                p.token[k0 + tid] = p.edge_tok[e];
+                p.node_new[k0 + tid] = p.edge_child[e];
+            } else {
+                p.token[k0 + tid] = v;
+            }
         } else {
             p.score_new[k0 + tid] = -__builtin_huge_valf();
             p.parent[k0 + tid] = -1;
             p.token[k0 + tid] = -1;
+            if (trie)
+                p.node_new[k0 + tid] = -1;
         }
     }
     for (int i = tid + NT; i < K; i += NT) {        // kept beyond K_max: padding
         p.score_new[k0 + i] = -__builtin_huge_valf();
         p.parent[k0 + i] = -1;
         p.token[k0 + i] = -1;
+        if (trie)
+            p.node_new[k0 + i] = -1;
     }
 }
 
@@ -791,18 +851,34 @@ size_t beam_select_workspace(int R_old, int K_max)
     auto al = [](size_t n) { return (n + 255) & ~(size_t)255; };
     const size_t R = static_cast<size_t>(R_old);
     return al(R * SEL_LIST * sizeof(uint64_t)) + al(R * sizeof(float)) +
-           al(R * sizeof(int32_t)) + al(R * static_cast<size_t>(K_max) * sizeof(uint64_t));
+           al(R * sizeof(int32_t)) + al(R * static_cast<size_t>(K_max) * sizeof(uint64_t)) +
+           2 * al(R * sizeof(int32_t));
 }
 
 hipError_t launch_beam_select(const SelParams &p, hipStream_t s)
 {
     if (p.R_old > 0) {
-        if (p.V <= 16 * SEL_ROW_THREADS)
-            hipLaunchKernelGGL(select_rows<16>, dim3(p.R_old), dim3(SEL_ROW_THREADS), 0, s, p);
-        else if (p.V <= 32 * SEL_ROW_THREADS)
-            hipLaunchKernelGGL(select_rows<32>, dim3(p.R_old), dim3(SEL_ROW_THREADS), 0, s, p);
-        else
-            hipLaunchKernelGGL(select_rows<64>, dim3(p.R_old), dim3(SEL_ROW_THREADS), 0, s, p);
+        const dim3 g(p.R_old), t(SEL_ROW_THREADS);
+        if (p.node_ptr) {
+            // sized by the largest fanout, which is usually far below V
+            const int f = p.max_fanout;
+            if (f <= SEL_ROW_THREADS)
+                hipLaunchKernelGGL((select_rows<1, true>), g, t, 0, s, p);
+            else if (f <= 4 * SEL_ROW_THREADS)
+                hipLaunchKernelGGL((select_rows<4, true>), g, t, 0, s, p);
+            else if (f <= 16 * SEL_ROW_THREADS)
+                hipLaunchKernelGGL((select_rows<16, true>), g, t, 0, s, p);
+            else if (f <= 32 * SEL_ROW_THREADS)
+                hipLaunchKernelGGL((select_rows<32, true>), g, t, 0, s, p);
+            else
+                hipLaunchKernelGGL((select_rows<64, true>), g, t, 0, s, p);
+        } else if (p.V <= 16 * SEL_ROW_THREADS) {
+            hipLaunchKernelGGL((select_rows<16, false>), g, t, 0, s, p);
+        } else if (p.V <= 32 * SEL_ROW_THREADS) {
+            hipLaunchKernelGGL((select_rows<32, false>), g, t, 0, s, p);
+        } else {
+            hipLaunchKernelGGL((select_rows<64, false>), g, t, 0, s, p);
+        }
     }
     if (p.B > 0)
         hipLaunchKernelGGL(select_request, dim3(p.B), dim3(SEL_REQ_THREADS), 0, s, p);

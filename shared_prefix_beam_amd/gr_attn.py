@@ -27,7 +27,7 @@ GR_ERR_DEVICE = -6
 
 EXPORTS = ("gr_decode_attn", "gr_decode_attn_generic", "gr_decode_attn_paged",
            "gr_check_metadata", "gr_beam_step", "gr_beam_select_workspace_bytes",
-           "gr_beam_select", "gr_status_str", "gr_version")
+           "gr_beam_select", "gr_beam_select_trie", "gr_status_str", "gr_version")
 
 
 class Dims(ctypes.Structure):
@@ -54,6 +54,15 @@ class SelectDims(ctypes.Structure):
 
     _fields_ = [("B", ctypes.c_int32), ("R_old", ctypes.c_int32), ("R_new", ctypes.c_int32),
                 ("V", ctypes.c_int32), ("K_max", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class SidTrie(ctypes.Structure):
+    """``gr_sid_trie`` (host memory holding device pointers)."""
+
+    _fields_ = [("node_ptr", ctypes.c_void_p), ("edge_tok", ctypes.c_void_p),
+                ("edge_child", ctypes.c_void_p), ("n_nodes", ctypes.c_int32),
+                ("n_edges", ctypes.c_int32), ("max_fanout", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class PagedCtx(ctypes.Structure):
@@ -99,6 +108,9 @@ def load() -> ctypes.CDLL:
         lib.gr_beam_select_workspace_bytes.restype = ctypes.c_size_t
         lib.gr_beam_select.argtypes = [SDP] + [P] * 8 + [ctypes.c_size_t, P]
         lib.gr_beam_select.restype = ctypes.c_int
+        lib.gr_beam_select_trie.argtypes = [SDP, ctypes.POINTER(SidTrie)] + [P] * 9 + \
+            [P, ctypes.c_size_t, P]
+        lib.gr_beam_select_trie.restype = ctypes.c_int
         lib.gr_status_str.argtypes = [ctypes.c_int]
         lib.gr_status_str.restype = ctypes.c_char_p
         lib.gr_version.argtypes = []
@@ -151,6 +163,15 @@ def gr_beam_select(dims: SelectDims, row_offset_old, row_offset_new, score_old, 
     return load().gr_beam_select(ctypes.byref(dims), row_offset_old, row_offset_new, score_old,
                                  logits, score_new, parent, token, workspace,
                                  int(workspace_bytes), stream)
+
+
+def gr_beam_select_trie(dims: SelectDims, trie: SidTrie, row_offset_old, row_offset_new,
+                        score_old, logits, node_old, score_new, parent, token, node_new,
+                        workspace, workspace_bytes: int, stream) -> int:
+    return load().gr_beam_select_trie(ctypes.byref(dims), ctypes.byref(trie), row_offset_old,
+                                      row_offset_new, score_old, logits, node_old, score_new,
+                                      parent, token, node_new, workspace, int(workspace_bytes),
+                                      stream)
 
 
 def gr_status_str(status: int) -> str:
@@ -400,3 +421,54 @@ def beam_select(row_offset_old, row_offset_new, score_old, logits, K_max: int, *
     if st != GR_OK:
         raise GrAttnError(st, "gr_beam_select")
     return score_new, parent, token
+
+
+def beam_select_trie(row_offset_old, row_offset_new, score_old, logits, node_old, node_ptr,
+                     edge_tok, edge_child, K_max: int, max_fanout: int, *, R_new=None,
+                     score_new=None, parent=None, token=None, node_new=None, workspace=None,
+                     stream=None):
+    """Item-constrained beam selection over a CSR semantic-ID trie
+    (include/gr_attn.h).  Returns (score_new, parent, token, node_new)."""
+    import torch
+    for name, t in (("node_old", node_old), ("node_ptr", node_ptr), ("edge_tok", edge_tok),
+                    ("edge_child", edge_child)):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device int32 tensor")
+    R_old, V = logits.shape
+    B = row_offset_old.numel() - 1
+    if R_new is None:
+        if score_new is None:
+            raise ValueError("pass R_new or the output tensors")
+        R_new = score_new.numel()
+    if node_old.numel() != R_old or edge_tok.numel() != edge_child.numel():
+        raise ValueError("node_old or edge tables mismatch")
+    dev = logits.device
+    if score_new is None:
+        score_new = torch.empty(R_new, dtype=torch.float32, device=dev)
+    if parent is None:
+        parent = torch.empty(R_new, dtype=torch.int32, device=dev)
+    if token is None:
+        token = torch.empty(R_new, dtype=torch.int32, device=dev)
+    if node_new is None:
+        node_new = torch.empty(R_new, dtype=torch.int32, device=dev)
+    for name, t, dt in (("row_offset_old", row_offset_old, torch.int32),
+                        ("row_offset_new", row_offset_new, torch.int32),
+                        ("score_old", score_old, torch.float32), ("logits", logits, torch.float32),
+                        ("score_new", score_new, torch.float32), ("parent", parent, torch.int32),
+                        ("token", token, torch.int32), ("node_new", node_new, torch.int32)):
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device {dt} tensor")
+    dims = SelectDims(B=B, R_old=R_old, R_new=R_new, V=V, K_max=int(K_max), reserved=0)
+    trie = SidTrie(node_ptr=_ptr(node_ptr), edge_tok=_ptr(edge_tok), edge_child=_ptr(edge_child),
+                   n_nodes=node_ptr.numel() - 1, n_edges=edge_tok.numel(),
+                   max_fanout=int(max_fanout), reserved=0)
+    ws_bytes = gr_beam_select_workspace_bytes(dims)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    st = gr_beam_select_trie(dims, trie, _ptr(row_offset_old), _ptr(row_offset_new),
+                             _ptr(score_old), _ptr(logits), _ptr(node_old), _ptr(score_new),
+                             _ptr(parent), _ptr(token), _ptr(node_new), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    if st != GR_OK:
+        raise GrAttnError(st, "gr_beam_select_trie")
+    return score_new, parent, token, node_new

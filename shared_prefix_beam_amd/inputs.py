@@ -490,6 +490,11 @@ class SidTrie:
     def n_edges(self) -> int:
         return int(self.edge_tok.size)
 
+    def level_fanout(self, d: int) -> int:
+        """Largest child count among the nodes of prefix length d."""
+        f = np.diff(self.node_ptr)[self.level_start[d]:self.level_start[d + 1]]
+        return int(f.max()) if f.size else 0
+
     def node_of(self, prefixes: np.ndarray) -> np.ndarray:
         """Node ids of prefixes [n][d] taken from the catalog (all of one
         length d); -1 for a prefix no item has."""

@@ -221,15 +221,17 @@ def select_call(dims, ws_bytes=None, **ptrs):
 
 
 def test_select_workspace_size():
-    # per row: a 32-key list (8 bytes each), its fp32 offset, an int32 slot and
-    # K_max survivor keys; four tables, each rounded up to 256 bytes
+    # per row: a 32-key list (8 bytes each), its fp32 offset, an int32 slot,
+    # K_max survivor keys, its candidate count and first trie edge; six
+    # tables, each rounded up to 256 bytes
     def al(n):
         return (n + 255) // 256 * 256
 
     for R, K in ((6, 5), (900, 900), (1, 1024)):
-        want = al(R * 32 * 8) + al(R * 4) + al(R * 4) + al(R * K * 8)
+        want = al(R * 32 * 8) + al(R * 4) + al(R * 4) + al(R * K * 8) + 2 * al(R * 4)
         assert gr_attn.gr_beam_select_workspace_bytes(select_dims(R_old=R, K_max=K)) == want
-    assert gr_attn.gr_beam_select_workspace_bytes(select_dims(R_old=900, K_max=900)) == 6718208
+    assert gr_attn.gr_beam_select_workspace_bytes(select_dims(R_old=900, K_max=900)) == \
+        6718208 + 2 * 3840
     assert gr_attn.gr_beam_select_workspace_bytes(select_dims(R_old=0)) == 0
     assert gr_attn.load().gr_beam_select_workspace_bytes(None) == 0
 
@@ -272,3 +274,55 @@ def test_select_misaligned_rejected(which, off):
 
 def test_select_empty_batch_is_a_no_op():
     assert select_call(select_dims(B=0, R_old=0, R_new=0)) == gr_attn.GR_OK
+
+
+# ---- gr_beam_select_trie host validation -----------------------------------
+def test_trie_struct_layout():
+    assert ctypes.sizeof(gr_attn.SidTrie) == 40
+
+
+def trie_desc(**over):
+    d = dict(node_ptr=P16, edge_tok=P16, edge_child=P16, n_nodes=10, n_edges=9, max_fanout=4,
+             reserved=0)
+    d.update(over)
+    return gr_attn.SidTrie(**d)
+
+
+def trie_call(dims, trie, **ptrs):
+    args = dict(ro_old=P16, ro_new=P16, score_old=P16, logits=P16, node_old=P16,
+                score_new=P16, parent=P16, token=P16, node_new=P16, workspace=P16)
+    args.update(ptrs)
+    return gr_attn.gr_beam_select_trie(dims, trie, args["ro_old"], args["ro_new"],
+                                       args["score_old"], args["logits"], args["node_old"],
+                                       args["score_new"], args["parent"], args["token"],
+                                       args["node_new"], args["workspace"],
+                                       gr_attn.gr_beam_select_workspace_bytes(dims), None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(n_nodes=0), gr_attn.GR_ERR_DIMS),
+    (dict(n_edges=-1), gr_attn.GR_ERR_DIMS),
+    (dict(max_fanout=0), gr_attn.GR_ERR_DIMS),
+    (dict(max_fanout=1001), gr_attn.GR_ERR_DIMS),
+    (dict(reserved=2), gr_attn.GR_ERR_DIMS),
+    (dict(node_ptr=None), gr_attn.GR_ERR_NULL),
+    (dict(edge_tok=None), gr_attn.GR_ERR_NULL),
+    (dict(edge_child=P16 + 2), gr_attn.GR_ERR_ALIGN),
+])
+def test_trie_bad_descriptor_rejected(over, code):
+    assert trie_call(select_dims(), trie_desc(**over)) == code
+
+
+@pytest.mark.parametrize("which", ["node_old", "node_new", "logits", "workspace"])
+def test_trie_null_pointer_rejected(which):
+    assert trie_call(select_dims(), trie_desc(), **{which: None}) == gr_attn.GR_ERR_NULL
+
+
+def test_trie_null_descriptor_rejected():
+    lib = gr_attn.load()
+    assert lib.gr_beam_select_trie(ctypes.byref(select_dims()), None, *([None] * 10), 0,
+                                   None) == gr_attn.GR_ERR_NULL
+
+
+def test_trie_empty_batch_is_a_no_op():
+    assert trie_call(select_dims(B=0, R_old=0, R_new=0), trie_desc()) == gr_attn.GR_OK
