@@ -36,6 +36,7 @@ constexpr int SEL_SURV_REG = 4;                           // survivors per threa
 constexpr int SEL_SURV_LDS = SEL_SURV_REG * SEL_REQ_THREADS;
 constexpr int SEL_REQ_NV = SEL_MAX_V / SEL_REQ_THREADS;   // logits per thread, re-selection
 constexpr int SEL_CAND = SEL_ROW_THREADS;                 // keys >= the row bound kept in LDS
+constexpr int SEL_WCAND = 256;                            // the same, one wave per row
 
 __device__ __forceinline__ uint32_t ord_f32(float f)
 {
@@ -248,42 +249,49 @@ __device__ __forceinline__ int wave_append(bool take, int *counter)
 }
 
 // Bitonic sort of one key per thread into descending order over threads
-// 0 .. ns-1 (ns a power of two <= NT; threads from ns on hold 0).  Stages
-// with partners 1, 2, 4, 8 lanes away exchange through DPP, 16 and 32
+// 0 .. ns-1 (ns a power of two <= NT; threads from ns on hold 0).  Each
+// stage is its own instantiation, so its partner distance J and block size
+// K are constants: 1, 2, 4 and 8 lanes away exchange through DPP, 16 and 32
 // through lane shuffles, wider ones through one of two LDS buffers in turn
-// (xch2: 2 x NT keys), one barrier each.
+// (xch2: 2 x NT keys), one barrier each.  A thread takes its partner's key
+// when (partner > own) matches (lower of the pair == block sorts descending).
+template <int NT, int K, int J>
+__device__ __forceinline__ void bitonic_stage(uint64_t &key, uint64_t *xch2, int &buf)
+{
+    const int tid = threadIdx.x;
+    uint64_t other;
+    if constexpr (J >= 64) {
+        uint64_t *x = xch2 + NT * buf;
+        x[tid] = key;
+        __syncthreads();
+        other = x[tid ^ J];
+        buf ^= 1;
+    } else if constexpr (J <= 8) {
+        other = dpp_xor_u64<J>(key);
+    } else {
+        other = shfl_xor_u64(key, J);
+    }
+    const bool same = ((tid & J) == 0) == ((tid & K) == 0);
+    key = ((other > key) == same) ? other : key;
+    if constexpr (J > 1)
+        bitonic_stage<NT, K, J / 2>(key, xch2, buf);
+}
+
+template <int NT, int K>
+__device__ __forceinline__ void bitonic_from(uint64_t &key, int ns, uint64_t *xch2, int &buf)
+{
+    if (K <= ns) {                                  // wave-uniform
+        bitonic_stage<NT, K, K / 2>(key, xch2, buf);
+        if constexpr (K < NT)
+            bitonic_from<NT, 2 * K>(key, ns, xch2, buf);
+    }
+}
+
 template <int NT>
 __device__ uint64_t block_sort_desc(uint64_t key, int ns, uint64_t *xch2)
 {
-    const int tid = threadIdx.x;
     int buf = 0;
-    for (int k = 2; k <= ns; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            uint64_t other;
-            if (j >= 64) {
-                uint64_t *x = xch2 + NT * buf;
-                x[tid] = key;
-                __syncthreads();
-                other = x[tid ^ j];
-                buf ^= 1;
-            } else if (j == 1) {
-                other = dpp_xor_u64<1>(key);
-            } else if (j == 2) {
-                other = dpp_xor_u64<2>(key);
-            } else if (j == 4) {
-                other = dpp_xor_u64<4>(key);
-            } else if (j == 8) {
-                other = dpp_xor_u64<8>(key);
-            } else {
-                other = shfl_xor_u64(key, j);
-            }
-            const bool desc = (tid & k) == 0;     // this block of k sorts descending
-            const bool lower = (tid & j) == 0;    // lower index of its pair
-            const uint64_t big = key > other ? key : other;
-            const uint64_t small = key > other ? other : key;
-            key = (lower == desc) ? big : small;
-        }
-    }
+    bitonic_from<NT, 2>(key, ns, xch2, buf);
     return key;
 }
 
@@ -514,6 +522,227 @@ __global__ __launch_bounds__(SEL_ROW_THREADS) void select_rows(const SelParams p
     }
 }
 
+__device__ __forceinline__ float wave_max(float v)
+{
+    for (int off = 32; off > 0; off >>= 1)
+        v = __builtin_fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+    for (int off = 32; off > 0; off >>= 1)
+        v += __shfl_xor(v, off);
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_i(int v)
+{
+    for (int off = 32; off > 0; off >>= 1)
+        v += __shfl_xor(v, off);
+    return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane)
+{
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(v, off);
+        if (lane >= off)
+            v += t;
+    }
+    return v;
+}
+
+// One beam row per wave, four rows per 256-thread workgroup, no block
+// barriers: candidate v = lane + 64 i (i < NL) sits in a register.  The
+// row's L best keys all have ordered value bits >= res, the L-th largest of
+// the 64 lane maxima (L distinct keys reach it), found by a 32-step ballot
+// search; the few keys above it are compacted in order into the wave's LDS
+// slice and ranked by counting.  With more than SEL_WCAND of them (ties at
+// the bound) the exact L-th largest value is searched instead and the ties
+// at it are taken in index order.
+template <int NL, bool TRIE>
+__global__ __launch_bounds__(256) void select_rows_wave(const SelParams p)
+{
+    __shared__ uint64_t cand_all[4][SEL_WCAND];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int r = blockIdx.x * 4 + wv;
+    if (r >= p.R_old)
+        return;
+    uint64_t *cand = cand_all[wv];
+    // the candidate chain (node, its edges, their logits) first: it does
+    // not depend on the request lookup, which overlaps with it
+    int n, e0;
+    row_candidates(p, r, TRIE, 64 * NL, n, e0);
+    const float *row = p.logits + (int64_t)r * p.V;
+    float x[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int v = lane + 64 * i;
+        int t = v;
+        if (TRIE && v < n)
+            t = p.edge_tok[e0 + v];
+        x[i] = (v < n && t >= 0 && t < p.V) ? row[t] : -__builtin_huge_valf();
+    }
+    const float score = p.score_old[r];
+    const int b = request_of(p.row_offset_old, p.B, r);
+    const int wl = r - p.row_offset_old[b];
+    int k_row = p.row_offset_new[b + 1] - p.row_offset_new[b];
+    k_row = k_row < p.V ? k_row : p.V;
+    k_row = k_row < p.K_max ? k_row : p.K_max;
+    if (k_row <= 0)
+        return;
+    const int L = k_row < SEL_LIST ? k_row : SEL_LIST;
+    if (lane == 0) {
+        p.ws_n[r] = n;
+        p.ws_e0[r] = e0;
+    }
+    uint64_t *list = p.ws_list + (int64_t)r * SEL_LIST;
+    if (n == 0) {                                 // no legal token: an empty list
+        if (lane < L)
+            list[lane] = 0;
+        return;
+    }
+    float m = x[0];
+#pragma unroll
+    for (int i = 1; i < NL; ++i)
+        m = __builtin_fmaxf(m, x[i]);
+    m = wave_max(m);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+        s += __expf(x[i] - m);
+    s = wave_sum(s);
+    const float off_w = score - (m + __logf(s));
+    if (lane == 0)
+        p.ws_off[r] = off_w;
+
+    // ordered value bits of candidate i, 0 when there is none (every real
+    // one is >= 1); rebuilt from x in each pass (an opaque copy of off_w
+    // keeps the compiler from holding all of them in registers)
+    struct Pass {
+        float ow;
+        int lim;                                  // candidates of this lane: v < n
+    };
+    auto ord_at = [&](int i, Pass q) -> uint32_t {
+        return 64 * i < q.lim ? ord_f32(q.ow + x[i]) : 0u;
+    };
+    auto fresh = [&]() {
+        Pass q{off_w, n - lane};
+        asm volatile("" : "+v"(q.ow), "+v"(q.lim));
+        return q;
+    };
+    uint32_t omax = 0;
+    {
+        const Pass ow = fresh();
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const uint32_t oi = ord_at(i, ow);
+            omax = oi > omax ? oi : omax;
+        }
+    }
+    const uint32_t flat0 = (uint32_t)wl * (uint32_t)p.V + (uint32_t)lane;
+    uint32_t res = 1;
+    if (n >= L) {                                 // min(n, 64) >= L lanes hold candidates
+        uint32_t acc = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t c = acc | (1u << bit);
+            if (__popcll(__ballot(omax >= c)) >= L)
+                acc = c;
+        }
+        res = acc > 1u ? acc : 1u;
+    }
+    int c = 0;
+    {
+        const Pass ow = fresh();
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+            c += ord_at(i, ow) >= res ? 1 : 0;
+    }
+    int incl = wave_incl_scan(c, lane);
+    int M = __shfl(incl, 63);
+    int n_keys = 0;                               // keys placed in cand
+    if (M <= SEL_WCAND) {
+        int at = incl - c;
+        const Pass ow = fresh();
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const uint32_t oi = ord_at(i, ow);
+            if (oi >= res)
+                cand[at++] = make_key(oi, flat0 + 64 * i);
+        }
+        n_keys = M;
+    } else {
+        // the exact L-th largest value (with repeats), bit by bit
+        uint32_t acc = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t t = acc | (1u << bit);
+            const Pass ow = fresh();
+            int k = 0;
+#pragma unroll
+            for (int i = 0; i < NL; ++i)
+                k += ord_at(i, ow) >= t ? 1 : 0;
+            if (wave_sum_i(k) >= L)
+                acc = t;
+        }
+        // everything above it, then the ties at it by increasing index
+        c = 0;
+        {
+            const Pass ow = fresh();
+#pragma unroll
+            for (int i = 0; i < NL; ++i)
+                c += ord_at(i, ow) > acc ? 1 : 0;
+        }
+        incl = wave_incl_scan(c, lane);
+        const int A = __shfl(incl, 63);           // < L
+        int at = incl - c;
+        const Pass ow = fresh();
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const uint32_t oi = ord_at(i, ow);
+            if (oi > acc)
+                cand[at++] = make_key(oi, flat0 + 64 * i);
+        }
+        int taken = 0;
+        const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            if (A + taken < L) {                  // wave-uniform: stop once L are placed
+                const uint32_t oi = ord_at(i, ow);
+                const bool tie = oi == acc;
+                const uint64_t bal = __ballot(tie);
+                const int rank = taken + __popcll(bal & below);
+                if (tie && A + rank < L)
+                    cand[A + rank] = make_key(oi, flat0 + 64 * i);
+                taken += __popcll(bal);
+            }
+        }
+        n_keys = L;
+    }
+    __builtin_amdgcn_wave_barrier();              // this wave's LDS writes precede its reads
+    // rank by counting; the L best land in the row's list in order
+    uint64_t mine[SEL_WCAND / 64];
+    int rk[SEL_WCAND / 64];
+#pragma unroll
+    for (int k = 0; k < SEL_WCAND / 64; ++k) {
+        mine[k] = lane + 64 * k < n_keys ? cand[lane + 64 * k] : 0;
+        rk[k] = 0;
+    }
+    for (int j = 0; j < n_keys; ++j) {
+        const uint64_t cj = cand[j];
+#pragma unroll
+        for (int k = 0; k < SEL_WCAND / 64; ++k)
+            rk[k] += cj > mine[k] ? 1 : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < SEL_WCAND / 64; ++k)
+        if (lane + 64 * k < n_keys && rk[k] < L)
+            list[rk[k]] = mine[k];
+    if (lane < L && lane >= n_keys)               // fewer candidates than L: pad
+        list[lane] = 0;
+}
+
 __global__ __launch_bounds__(SEL_REQ_THREADS) void select_request(const SelParams p)
 {
     constexpr int NT = SEL_REQ_THREADS, NW = NT / 64;
@@ -524,6 +753,7 @@ __global__ __launch_bounds__(SEL_REQ_THREADS) void select_request(const SelParam
     __shared__ uint32_t hist3[3 * 256];
     __shared__ uint64_t red64a[2 * NW], red64b[2 * NW];
     __shared__ int redi[NW], wsum[NW];
+    __shared__ int wcnt[1][NW];
     __shared__ int cnt_lds[NT];
     __shared__ uint64_t xch2[2 * NT];
     __shared__ uint64_t surv_lds[SEL_SURV_LDS];
@@ -615,15 +845,74 @@ __global__ __launch_bounds__(SEL_REQ_THREADS) void select_request(const SelParam
                     f(head_key(i));
             }
         };
-        uint64_t kmax = 0, kmin = ~0ull;
-        visit([&](uint64_t key) {
-            kmax = key > kmax ? key : kmax;
-            kmin = key < kmin ? key : kmin;
-        });
-        block_minmax<NT>(kmax, kmin, red64a);
-        uint64_t pf, mk;
-        radix_kth<NT>(K_eff, kmax, kmin, visit, hist3, hb, pf, mk);
-        tau = pf;                                   // the K_eff selected keys are >= pf
+        if (mode == 2) {
+            uint64_t kmax = 0, kmin = ~0ull;
+            visit([&](uint64_t key) {
+                kmax = key > kmax ? key : kmax;
+                kmin = key < kmin ? key : kmin;
+            });
+            block_minmax<NT>(kmax, kmin, red64a);
+            uint64_t pf, mk;
+            radix_kth<NT>(K_eff, kmax, kmin, visit, hist3, hb, pf, mk);
+            tau = pf;                               // the K_eff selected keys are >= pf
+        } else {
+            // Each wave bounds its own share: with n_w of the n_head keys it
+            // finds the q_w-th largest ordered value among them, q_w =
+            // ceil(K_eff * n_w / n_head), bit by bit with ballots (no
+            // barrier).  The q_w sum to at least K_eff, so the smallest of
+            // the waves' values has K_eff distinct keys at or above it.
+            int n_w = 0;
+            uint32_t hmax = 0, hmin = ~0u;
+            visit([&](uint64_t key) {
+                const uint32_t h = (uint32_t)(key >> 32);
+                hmax = h > hmax ? h : hmax;
+                hmin = h < hmin ? h : hmin;
+                ++n_w;
+            });
+            n_w = wave_sum_i(n_w);
+            for (int off = 32; off > 0; off >>= 1) {
+                const uint32_t a2 = __shfl_xor(hmax, off), c2 = __shfl_xor(hmin, off);
+                hmax = a2 > hmax ? a2 : hmax;
+                hmin = c2 < hmin ? c2 : hmin;
+            }
+            const int q = n_w ? (int)(((int64_t)K_eff * n_w + n_head - 1) / n_head) : 0;
+            uint32_t acc = ~0u;                     // no keys: no constraint
+            if (q > 0) {
+                const uint32_t d = hmax ^ hmin;
+                const int top = d ? 31 - __clz(d) : -1;
+                // the shared prefix with zeros below: every key reaches it
+                acc = top < 0 ? hmax : (top >= 31 ? 0u : (hmax & ~((2u << top) - 1u)));
+                for (int bit = top; bit >= 0; --bit) {
+                    const uint32_t t = acc | (1u << bit);
+                    int cnt = 0;                    // wave-uniform: ballot popcounts
+                    if (mode == 0) {
+#pragma unroll
+                        for (int i = 0; i < LOADS; ++i) {
+                            const bool in = wv * WROWS + i * RPL + g < W;
+                            cnt += __popcll(__ballot(in && 2 * kp < head &&
+                                                     (uint32_t)(ka[i] >> 32) >= t));
+                            cnt += __popcll(__ballot(in && 2 * kp + 1 < head &&
+                                                     (uint32_t)(kb[i] >> 32) >= t));
+                        }
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < SEL_HEAD_REG; ++j)
+                            cnt += __popcll(__ballot(tid + NT * j < n_head &&
+                                                     (uint32_t)(hk[j] >> 32) >= t));
+                    }
+                    if (cnt >= q)
+                        acc = t;
+                }
+            }
+            if (lane == 0)
+                wcnt[0][wv] = (int)acc;
+            __syncthreads();
+            uint32_t lo = ~0u;
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+                lo = (uint32_t)wcnt[0][w] < lo ? (uint32_t)wcnt[0][w] : lo;
+            tau = (uint64_t)lo << 32;
+        }
     }
     tau = tau > 1 ? tau : 1;                        // every real key is >= 1; 0 pads
 
@@ -858,23 +1147,25 @@ size_t beam_select_workspace(int R_old, int K_max)
 hipError_t launch_beam_select(const SelParams &p, hipStream_t s)
 {
     if (p.R_old > 0) {
-        const dim3 g(p.R_old), t(SEL_ROW_THREADS);
+        // one wave per row up to 64 * 16 candidates (short rows: latency of
+        // the dependent loads dominates), else one workgroup per row (long
+        // rows: a wave holding 64 * 32 or more keys runs at low occupancy)
+        const int n = p.node_ptr ? p.max_fanout : p.V;
+        const dim3 gw((p.R_old + 3) / 4), g(p.R_old), t(SEL_ROW_THREADS);
         if (p.node_ptr) {
-            // sized by the largest fanout, which is usually far below V
-            const int f = p.max_fanout;
-            if (f <= SEL_ROW_THREADS)
-                hipLaunchKernelGGL((select_rows<1, true>), g, t, 0, s, p);
-            else if (f <= 4 * SEL_ROW_THREADS)
-                hipLaunchKernelGGL((select_rows<4, true>), g, t, 0, s, p);
-            else if (f <= 16 * SEL_ROW_THREADS)
-                hipLaunchKernelGGL((select_rows<16, true>), g, t, 0, s, p);
-            else if (f <= 32 * SEL_ROW_THREADS)
+            if (n <= 64 * 4)
+                hipLaunchKernelGGL((select_rows_wave<4, true>), gw, t, 0, s, p);
+            else if (n <= 64 * 16)
+                hipLaunchKernelGGL((select_rows_wave<16, true>), gw, t, 0, s, p);
+            else if (n <= 32 * SEL_ROW_THREADS)
                 hipLaunchKernelGGL((select_rows<32, true>), g, t, 0, s, p);
             else
                 hipLaunchKernelGGL((select_rows<64, true>), g, t, 0, s, p);
-        } else if (p.V <= 16 * SEL_ROW_THREADS) {
-            hipLaunchKernelGGL((select_rows<16, false>), g, t, 0, s, p);
-        } else if (p.V <= 32 * SEL_ROW_THREADS) {
+        } else if (n <= 64 * 4) {
+            hipLaunchKernelGGL((select_rows_wave<4, false>), gw, t, 0, s, p);
+        } else if (n <= 64 * 16) {
+            hipLaunchKernelGGL((select_rows_wave<16, false>), gw, t, 0, s, p);
+        } else if (n <= 32 * SEL_ROW_THREADS) {
             hipLaunchKernelGGL((select_rows<32, false>), g, t, 0, s, p);
         } else {
             hipLaunchKernelGGL((select_rows<64, false>), g, t, 0, s, p);
