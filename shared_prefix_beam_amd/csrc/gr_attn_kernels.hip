@@ -30,9 +30,11 @@
 //     stays fixed during the context sweep (the first tile's maximum), so the
 //     O^T accumulators are written only by the matrix cores inside the loop;
 //     a second, exact sweep runs only if a row sum leaves the safe range.
-//   * BeamKV steps are spread over the key streams; each stream folds its
-//     steps into its own (max, sum, O) with vector loads along the BeamPath,
-//     before the streams merge through LDS by log-sum-exp.
+//   * BeamKV steps are spread over the key streams; before its context
+//     sweep, each stream folds its steps into its own (max, sum, O) from
+//     rows gathered along the BeamPath into the still empty tile ring; that
+//     partial seeds the accumulators, and the streams merge through LDS by
+//     log-sum-exp at the end.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -52,6 +54,7 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int KT = 32;          // keys per context tile
 constexpr int PSTEPS = 4;       // beam steps gathered into LDS at a time, at most
+constexpr int PTAB_BYTES = 4096;  // LDS for the BeamPath entries of a workgroup's beams
 constexpr float SAFE_SUM = 1.8446744e19f;  // 2^64: largest row sum accepted in pass 0
 constexpr float NEG_INF = -__builtin_huge_valf();
 constexpr uint32_t BF16_ONES = 0x3f803f80u;  // two bf16 ones
@@ -78,12 +81,19 @@ __device__ __forceinline__ int kswz(int r) { return r & (D / 8 - 1); }
 template <int D>
 __device__ __forceinline__ int vswz(int r) { return (4 * (r & 3)) & (D / 8 - 1); }
 
+// LDS of the fused kernel: the tile ring (reused by the beam gathers and
+// the merge of the key streams), then the staged BeamPath entries.
 template <int D, int NQT, int NKS, int NBUF>
-constexpr int lds_bytes()
+constexpr int lds_main()
 {
     constexpr int stage = NKS * NBUF * Geo<D>::TILE;
     constexpr int merge = (NKS - 1) * NQT * Geo<D>::OSLOT;
     return stage > merge ? stage : merge;
+}
+template <int D, int NQT, int NKS, int NBUF>
+constexpr int lds_bytes()
+{
+    return lds_main<D, NQT, NKS, NBUF>() + PTAB_BYTES;
 }
 
 // One 1 KB direct global->LDS load: lane i of the wave writes bytes
@@ -232,11 +242,38 @@ void fused_decode_attn(const Params p)
 #pragma unroll
         for (int c = 0; c < Gm::DC; ++c)
             qf[c] = qvalid ? ldg16(src + 16 * c) : u32x4{0, 0, 0, 0};
-        // consume the loads here, so that no wait for them is left inside
-        // the tile loop (where it would also wait for the tile prefetches)
+    }
+
+    // ---- BeamPath entries of the workgroup's beams, staged in LDS ---------
+    // Loaded with Q, so that the beam stage after the context sweep finds
+    // its gather indices in LDS instead of waiting on memory for them.  The
+    // tile's beam beta (beam tile_row0/G + beta) keeps step s at entry
+    // beta*T + s; entries of beams past the request's last are 0.
+    constexpr int NTHR = 64 * NQT * NKS;
+    constexpr int PT_PER = (PTAB_BYTES / 4 + NTHR - 1) / NTHR;
+    int32_t *const ptab_l = reinterpret_cast<int32_t *>(smem + lds_main<D, NQT, NKS, NBUF>());
+    const int nb_wg = (32 * NQT) / G;             // the tile's beams (G divides 32)
+    const bool use_tab = (32 % G == 0) && T > 0 && nb_wg * T * 4 <= PTAB_BYTES;
+    const int beam0 = tile_row0 / G;
+    int ptv[PT_PER];
 #pragma unroll
-        for (int c = 0; c < Gm::DC; ++c)
-            asm volatile("" : "+v"(qf[c]));
+    for (int i = 0; i < PT_PER; ++i) {
+        const int e = tid + i * NTHR;
+        const int beta = use_tab ? e / T : 0;
+        const int sidx = e - beta * T;
+        const bool ok = use_tab && e < nb_wg * T && beam0 + beta < Wb;
+        ptv[i] = ok ? p.beam_path[(int64_t)(r0 + beam0 + beta) * p.T_cap + sidx] : 0;
+    }
+    // consume the loads here, so that no wait for them is left inside the
+    // tile loop (where it would also wait for the tile prefetches)
+#pragma unroll
+    for (int c = 0; c < Gm::DC; ++c)
+        asm volatile("" : "+v"(qf[c]));
+#pragma unroll
+    for (int i = 0; i < PT_PER; ++i) {
+        const int e = tid + i * NTHR;
+        if (use_tab && e < nb_wg * T)
+            ptab_l[e] = ptv[i];                    // read after the next barrier
     }
 
     float m_ref = NEG_INF;                        // reference maximum, log2 units
@@ -247,9 +284,12 @@ void fused_decode_attn(const Params p)
     float l_run = 0.f;
     float l_lse = 0.f;
     f32x16 acc[Gm::DB];
+    f32x16 o[Gm::DB];                             // vector-unit copy (beam stage, merge)
 #pragma unroll
-    for (int db = 0; db < Gm::DB; ++db)
+    for (int db = 0; db < Gm::DB; ++db) {
         acc[db] = f32x16{};
+        o[db] = f32x16{};
+    }
     const float cs = p.scale_log2;
 
     // ---- shared (context) stage -----------------------------------------
@@ -595,9 +635,23 @@ void fused_decode_attn(const Params p)
                     for (int r = 1; r < 16; ++r)
                         mx = __builtin_fmaxf(mx, s_cur[r]);
                     mx = __builtin_fmaxf(mx, swap32(mx, h));
-                    m_ref = __builtin_fmaxf(m_ref, mx * cs);
+                    // the beam partial, folded before the sweep, moves to
+                    // the sweep's reference and seeds the accumulators
+                    const float m_new = __builtin_fmaxf(m_ref, mx * cs);
+                    const float a = m_ref == NEG_INF ? 0.f : exp2_fast(m_ref - m_new);
+                    l_run *= a;
+                    l_lse *= a;
+#pragma unroll
+                    for (int db = 0; db < Gm::DB; ++db)
+                        acc[db] = o[db] * a;
+                    m_ref = m_new;
                 }
             } else {
+                if (first_max) {
+#pragma unroll
+                    for (int db = 0; db < Gm::DB; ++db)
+                        acc[db] = o[db];
+                }
                 block_barrier();
             }
             // one pipelined iteration; HAS_NEXT (compile time) keeps the
@@ -693,43 +747,15 @@ void fused_decode_attn(const Params p)
         block_barrier();                           // buffers free for the next user
     };
 
-    // Pass 0 takes each stream's first-tile maximum as the fixed reference:
-    // later tiles may exceed it, so probabilities can grow past 1.  As long
-    // as every row sum stays below 2^64 nothing can overflow and the final
-    // normalisation is exact.  Otherwise (scores rising by more than ~44
-    // nats along the context) the workgroup sweeps again: exact maxima
-    // first, then the accumulation against them.
-    sweep_acc(true);
-    if (__syncthreads_or(qvalid && !(l_lse < SAFE_SUM))) {
-        m_ref = NEG_INF;
-        l_run = 0.f;
-        l_lse = 0.f;
-#pragma unroll
-        for (int db = 0; db < Gm::DB; ++db)
-            acc[db] = f32x16{};
-        sweep(true, std::false_type{});
-        sweep_acc(false);
-    }
-
-    // The vector-unit stages below work on a copy of the accumulators pinned
-    // in ordinary VGPRs; the context loop above then keeps its accumulators
-    // in the matrix cores' accumulation registers without per-iteration moves.
-    f32x16 o[Gm::DB];
-#pragma unroll
-    for (int db = 0; db < Gm::DB; ++db) {
-        o[db] = acc[db];
-        asm volatile("" : "+v"(o[db]));
-    }
-
     // ---- per-beam stage: BeamKV steps ks, ks+NKS, ... along BeamPath ------
     // Each lane folds the K and V rows of its query's path token for a step
     // into its (max, sums, O) online.  When G divides 32 the 32/G beams of a
-    // wave are gathered first into the (now free) tile buffers with direct
-    // loads, each covering whole rows (a 1 KB load takes 1024/ROW rows: few
-    // cache lines per instruction), up to `sch` steps at a time; row beta's
-    // 16-byte chunks sit at slot chunk ^ (beta & (CH-1)).  The path entry of
-    // beam beta is the one lane beta*G fetched with Q.  Otherwise each lane
-    // loads its rows from memory.
+    // wave are gathered first into the (still unused) tile buffers with
+    // direct loads, each covering whole rows (a 1 KB load takes 1024/ROW
+    // rows: few cache lines per instruction), up to `sch` steps at a time;
+    // row beta's 16-byte chunks sit at slot chunk ^ (beta & (CH-1)).  The
+    // path entries come from the staged table (else from the lane beta*G,
+    // which loads its own).  Otherwise each lane loads its rows from memory.
     const int n_steps = T > ks ? (T - ks + NKS - 1) / NKS : 0;
     auto step_idx = [&](int i) __attribute__((always_inline)) {
         int qr = qrow;
@@ -767,84 +793,142 @@ void fused_decode_attn(const Params p)
     const int sb = 2 * nb * Gm::ROW;               // LDS bytes per gathered step
     const int fit = RING / (NQT * NKS * sb);
     const int sch = (32 % G == 0) ? (fit < PSTEPS ? fit : PSTEPS) : 0;
-    if (wave_live && sch > 0) {
-        const uint32_t area = lds0 + wave * sch * sb;
-        const char *area_p = smem + wave * sch * sb;
-        const int lpr = nb * Gm::ROW / 1024;       // 1 KB loads per step for K (and V)
-        const int beta_l = lane / Gm::CH;
-        const int beta_q = c32 / G;                // this lane's beam within the wave
-        const int sw = beta_q & (Gm::CH - 1);
-        const uint16_t *bk = p.beam_k + ((int64_t)b * p.beam_cap * p.Hkv + g) * D;
-        const uint16_t *bv = p.beam_v + ((int64_t)b * p.beam_cap * p.Hkv + g) * D;
-        constexpr int MAXL = 32 * Gm::ROW / 1024;  // 1 KB loads per step at G = 1
-        for (int s0 = 0; s0 < n_steps; s0 += sch) {
-            const int cnt = sch < n_steps - s0 ? sch : n_steps - s0;
-            // path entries of the chunk's steps: one load per lane and step,
-            // then the shuffles to the rows each lane's direct loads cover,
-            // all before the first direct load
-            int myidx[PSTEPS];
+    auto beam_stage = [&]() __attribute__((always_inline)) {
+        if (wave_live && sch > 0) {
+            const uint32_t area = lds0 + wave * sch * sb;
+            const char *area_p = smem + wave * sch * sb;
+            const int lpr = nb * Gm::ROW / 1024;       // 1 KB loads per step for K (and V)
+            const int beta_l = lane / Gm::CH;
+            const int beta_q = c32 / G;                // this lane's beam within the wave
+            const int sw = beta_q & (Gm::CH - 1);
+            const uint16_t *bk = p.beam_k + ((int64_t)b * p.beam_cap * p.Hkv + g) * D;
+            const uint16_t *bv = p.beam_v + ((int64_t)b * p.beam_cap * p.Hkv + g) * D;
+            constexpr int MAXL = 32 * Gm::ROW / 1024;  // 1 KB loads per step at G = 1
+            const int tb_w = qt * nb;                  // the wave's first beam in the table
+            for (int s0 = 0; s0 < n_steps; s0 += sch) {
+                const int cnt = sch < n_steps - s0 ? sch : n_steps - s0;
+                // path entries of the chunk's steps for the rows each lane's
+                // direct loads cover: from the staged table, or one global load
+                // per lane and step followed by shuffles; all before the first
+                // direct load
+                int rid[PSTEPS][MAXL];
+                if (use_tab) {
 #pragma unroll
-            for (int i = 0; i < PSTEPS; ++i)
-                myidx[i] = i < cnt ? step_idx(s0 + i) : 0;
-            int rid[PSTEPS][MAXL];
+                    for (int i = 0; i < PSTEPS; ++i)
 #pragma unroll
-            for (int i = 0; i < PSTEPS; ++i)
+                        for (int u = 0; u < MAXL; ++u) {
+                            const int beta = u * (1024 / Gm::ROW) + beta_l;
+                            rid[i][u] = (i < cnt && u < lpr)
+                                            ? ptab_l[(tb_w + beta) * T + ks + (s0 + i) * NKS]
+                                            : 0;
+                        }
+                } else {
+                    int myidx[PSTEPS];
 #pragma unroll
-                for (int u = 0; u < MAXL; ++u) {
-                    const int beta = u * (1024 / Gm::ROW) + beta_l;
-                    rid[i][u] = (i < cnt && u < lpr) ? __shfl(myidx[i], beta * G) : 0;
+                    for (int i = 0; i < PSTEPS; ++i)
+                        myidx[i] = i < cnt ? step_idx(s0 + i) : 0;
+#pragma unroll
+                    for (int i = 0; i < PSTEPS; ++i)
+#pragma unroll
+                        for (int u = 0; u < MAXL; ++u) {
+                            const int beta = u * (1024 / Gm::ROW) + beta_l;
+                            rid[i][u] = (i < cnt && u < lpr) ? __shfl(myidx[i], beta * G) : 0;
+                        }
                 }
 #pragma unroll
-            for (int i = 0; i < PSTEPS; ++i)
+                for (int i = 0; i < PSTEPS; ++i)
 #pragma unroll
-                for (int u = 0; u < MAXL; ++u)
-                    if (i < cnt && u < lpr) {
-                        const int beta = u * (1024 / Gm::ROW) + beta_l;
-                        const int64_t src = (int64_t)rid[i][u] * p.Hkv * D +
-                                            8 * ((lane % Gm::CH) ^ (beta & (Gm::CH - 1)));
-                        const uint32_t dst = area + i * sb + u * 1024;
-                        dma16(bk + src, dst);
-                        dma16(bv + src, dst + nb * Gm::ROW);
-                    }
-            wait_vm<0>();
-            for (int i = 0; i < cnt; ++i) {
-                const char *krow = area_p + i * sb + beta_q * Gm::ROW;
-                const char *vrow = krow + nb * Gm::ROW;
+                    for (int u = 0; u < MAXL; ++u)
+                        if (i < cnt && u < lpr) {
+                            const int beta = u * (1024 / Gm::ROW) + beta_l;
+                            const int64_t src = (int64_t)rid[i][u] * p.Hkv * D +
+                                                8 * ((lane % Gm::CH) ^ (beta & (Gm::CH - 1)));
+                            const uint32_t dst = area + i * sb + u * 1024;
+                            dma16(bk + src, dst);
+                            dma16(bv + src, dst + nb * Gm::ROW);
+                        }
+                wait_vm<0>();
+                for (int i = 0; i < cnt; ++i) {
+                    const char *krow = area_p + i * sb + beta_q * Gm::ROW;
+                    const char *vrow = krow + nb * Gm::ROW;
+                    u32x4 kr[Gm::DC];
+                    u32x2 vr[Gm::DB][4];
+#pragma unroll
+                    for (int c = 0; c < Gm::DC; ++c)
+                        kr[c] = *reinterpret_cast<const u32x4 *>(krow + 16 * ((2 * c + h) ^ sw));
+#pragma unroll
+                    for (int db = 0; db < Gm::DB; ++db)
+#pragma unroll
+                        for (int rg = 0; rg < 4; ++rg)
+                            vr[db][rg] = *reinterpret_cast<const u32x2 *>(
+                                vrow + 16 * ((4 * db + rg) ^ sw) + 8 * h);
+                    fold(kr, vr);
+                }
+                // this wave's reads of the area are done before it is refilled
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            }
+        } else if (wave_live) {
+            for (int i = 0; i < n_steps; ++i) {
+                const int idx = step_idx(i);
+                const int64_t base = (((int64_t)b * p.beam_cap + idx) * p.Hkv + g) * D;
+                const uint16_t *kp = p.beam_k + base + 8 * h;
+                const uint16_t *vp = p.beam_v + base + 4 * h;
                 u32x4 kr[Gm::DC];
                 u32x2 vr[Gm::DB][4];
 #pragma unroll
                 for (int c = 0; c < Gm::DC; ++c)
-                    kr[c] = *reinterpret_cast<const u32x4 *>(krow + 16 * ((2 * c + h) ^ sw));
+                    kr[c] = qvalid ? ldg16(kp + 16 * c) : u32x4{0, 0, 0, 0};
 #pragma unroll
                 for (int db = 0; db < Gm::DB; ++db)
 #pragma unroll
                     for (int rg = 0; rg < 4; ++rg)
-                        vr[db][rg] = *reinterpret_cast<const u32x2 *>(
-                            vrow + 16 * ((4 * db + rg) ^ sw) + 8 * h);
+                        vr[db][rg] = qvalid ? ldg8(vp + 32 * db + 8 * rg) : u32x2{0, 0};
                 fold(kr, vr);
             }
-            // this wave's reads of the area are done before it is refilled
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
-    } else if (wave_live) {
-        for (int i = 0; i < n_steps; ++i) {
-            const int idx = step_idx(i);
-            const int64_t base = (((int64_t)b * p.beam_cap + idx) * p.Hkv + g) * D;
-            const uint16_t *kp = p.beam_k + base + 8 * h;
-            const uint16_t *vp = p.beam_v + base + 4 * h;
-            u32x4 kr[Gm::DC];
-            u32x2 vr[Gm::DB][4];
+    };
+
+    // The BeamKV steps are folded first, while the tile ring is still empty:
+    // their gathers overlap the start of the other workgroups' sweeps, and
+    // the partial seeds the accumulators at the first tile, rescaled to the
+    // sweep's reference.
+    block_barrier();                               // staged BeamPath entries written
+    beam_stage();
+    block_barrier();                               // gather area read before the tiles land
+
+    // Pass 0 takes the larger of the beam partial's maximum and each
+    // stream's first-tile maximum as the fixed reference:
+    // later tiles may exceed it, so probabilities can grow past 1.  As long
+    // as every row sum stays below 2^64 nothing can overflow and the final
+    // normalisation is exact.  Otherwise (scores rising by more than ~44
+    // nats along the context) the workgroup sweeps again: exact maxima
+    // first, then the accumulation against them.
+    // The re-sweep starts from nothing and folds the BeamKV steps again
+    // after it.
+    sweep_acc(true);
+    bool beam_again = false;
+    if (__syncthreads_or(qvalid && !(l_lse < SAFE_SUM))) {
+        beam_again = true;                         // the beam partial is dropped with the rest
+        m_ref = NEG_INF;
+        l_run = 0.f;
+        l_lse = 0.f;
 #pragma unroll
-            for (int c = 0; c < Gm::DC; ++c)
-                kr[c] = qvalid ? ldg16(kp + 16 * c) : u32x4{0, 0, 0, 0};
-#pragma unroll
-            for (int db = 0; db < Gm::DB; ++db)
-#pragma unroll
-                for (int rg = 0; rg < 4; ++rg)
-                    vr[db][rg] = qvalid ? ldg8(vp + 32 * db + 8 * rg) : u32x2{0, 0};
-            fold(kr, vr);
-        }
+        for (int db = 0; db < Gm::DB; ++db)
+            acc[db] = f32x16{};
+        sweep(true, std::false_type{});
+        sweep_acc(false);
     }
+
+    // The vector-unit stages below work on a copy of the accumulators pinned
+    // in ordinary VGPRs; the context loop above then keeps its accumulators
+    // in the matrix cores' accumulation registers without per-iteration moves.
+#pragma unroll
+    for (int db = 0; db < Gm::DB; ++db) {
+        o[db] = acc[db];
+        asm volatile("" : "+v"(o[db]));
+    }
+    if (beam_again)
+        beam_stage();
     if constexpr (NKS > 1)
         block_barrier();                           // gathered rows read before the merge
     // full row sums (the two lane halves held different keys)
