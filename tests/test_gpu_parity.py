@@ -103,6 +103,34 @@ def test_rising_scores_take_exact_sweep():
     assert_parity(out, lse, ref_out, ref_lse, "rising")
 
 
+def test_beam_dominant_and_context_dominant_rows():
+    """The BeamKV partial, folded before the context sweep, seeds the
+    accumulators after a rescale to the sweep's reference.  Request 0: each
+    beam's current token has K = 3 q for the group's first head, so that
+    head's beam scores exceed every context score by tens of nats (the
+    reference is the beam maximum).  Request 1: beam keys -3 q, scores far
+    below the context (the beam partial is rescaled by a tiny factor)."""
+    inp = I.custom(B=2, Hq=16, Hkv=8, D=128, W=[40, 20], ctx_len=[700, 300], beam_len=[3, 2],
+                   seed=31)
+    G = inp.wl.Hq // inp.wl.Hkv
+    q = I.bf16_bits_to_f32(inp.q)
+    bk = I.bf16_bits_to_f32(inp.beam_k).copy()
+    for b, sign in ((0, 3.0), (1, -3.0)):
+        T = int(inp.beam_len[b])
+        for r in range(int(inp.row_offset[b]), int(inp.row_offset[b + 1])):
+            for s in range(T):
+                p = int(inp.beam_path[r, s])
+                if b == 0 and s < T - 1:
+                    continue                       # request 0: only the current token
+                for g in range(inp.wl.Hkv):
+                    bk[b, p, g, :] = sign * q[r, g * G, :]
+    inp.beam_k[:] = I.to_bf16_bits(bk)
+    log("[parity] beam-dominant and context-dominant rows")
+    out, lse = run_lib(inp)
+    ref_out, ref_lse = O.decode_attn_inputs(inp)
+    assert_parity(out, lse, ref_out, ref_lse, "beam/context dominance")
+
+
 def test_explicit_scale():
     inp = I.custom(B=2, Hq=16, Hkv=8, D=128, W=[10, 7], ctx_len=[200, 90], beam_len=[3, 2],
                    seed=17)
