@@ -761,7 +761,6 @@ __global__ __launch_bounds__(SEL_REQ_THREADS) void select_request(const SelParam
     __shared__ uint32_t hist3[3 * 256];
     __shared__ uint64_t red64a[2 * NW], red64b[2 * NW];
     __shared__ int redi[NW], wsum[NW];
-    __shared__ int wcnt[1][NW];
     __shared__ int cnt_lds[NT];
     __shared__ uint64_t xch2[2 * NT];
     __shared__ uint64_t surv_lds[SEL_SURV_LDS];
@@ -853,74 +852,21 @@ __global__ __launch_bounds__(SEL_REQ_THREADS) void select_request(const SelParam
                     f(head_key(i));
             }
         };
-        if (mode == 2) {
-            uint64_t kmax = 0, kmin = ~0ull;
-            visit([&](uint64_t key) {
-                kmax = key > kmax ? key : kmax;
-                kmin = key < kmin ? key : kmin;
-            });
-            block_minmax<NT>(kmax, kmin, red64a);
-            uint64_t pf, mk;
-            radix_kth<NT>(K_eff, kmax, kmin, visit, hist3, hb, pf, mk);
-            tau = pf;                               // the K_eff selected keys are >= pf
-        } else {
-            // Each wave bounds its own share: with n_w of the n_head keys it
-            // finds the q_w-th largest ordered value among them, q_w =
-            // ceil(K_eff * n_w / n_head), bit by bit with ballots (no
-            // barrier).  The q_w sum to at least K_eff, so the smallest of
-            // the waves' values has K_eff distinct keys at or above it.
-            int n_w = 0;
-            uint32_t hmax = 0, hmin = ~0u;
-            visit([&](uint64_t key) {
-                const uint32_t h = (uint32_t)(key >> 32);
-                hmax = h > hmax ? h : hmax;
-                hmin = h < hmin ? h : hmin;
-                ++n_w;
-            });
-            n_w = wave_sum_i(n_w);
-            for (int off = 32; off > 0; off >>= 1) {
-                const uint32_t a2 = __shfl_xor(hmax, off), c2 = __shfl_xor(hmin, off);
-                hmax = a2 > hmax ? a2 : hmax;
-                hmin = c2 < hmin ? c2 : hmin;
-            }
-            const int q = n_w ? (int)(((int64_t)K_eff * n_w + n_head - 1) / n_head) : 0;
-            uint32_t acc = ~0u;                     // no keys: no constraint
-            if (q > 0) {
-                const uint32_t d = hmax ^ hmin;
-                const int top = d ? 31 - __clz(d) : -1;
-                // the shared prefix with zeros below: every key reaches it
-                acc = top < 0 ? hmax : (top >= 31 ? 0u : (hmax & ~((2u << top) - 1u)));
-                for (int bit = top; bit >= 0; --bit) {
-                    const uint32_t t = acc | (1u << bit);
-                    int cnt = 0;                    // wave-uniform: ballot popcounts
-                    if (mode == 0) {
-#pragma unroll
-                        for (int i = 0; i < LOADS; ++i) {
-                            const bool in = wv * WROWS + i * RPL + g < W;
-                            cnt += __popcll(__ballot(in && 2 * kp < head &&
-                                                     (uint32_t)(ka[i] >> 32) >= t));
-                            cnt += __popcll(__ballot(in && 2 * kp + 1 < head &&
-                                                     (uint32_t)(kb[i] >> 32) >= t));
-                        }
-                    } else {
-#pragma unroll
-                        for (int j = 0; j < SEL_HEAD_REG; ++j)
-                            cnt += __popcll(__ballot(tid + NT * j < n_head &&
-                                                     (uint32_t)(hk[j] >> 32) >= t));
-                    }
-                    if (cnt >= q)
-                        acc = t;
-                }
-            }
-            if (lane == 0)
-                wcnt[0][wv] = (int)acc;
-            __syncthreads();
-            uint32_t lo = ~0u;
-#pragma unroll
-            for (int w = 0; w < NW; ++w)
-                lo = (uint32_t)wcnt[0][w] < lo ? (uint32_t)wcnt[0][w] : lo;
-            tau = (uint64_t)lo << 32;
-        }
+        // the K_eff-th best head key, exactly, by radix select over the
+        // keys where they sit (registers or memory); the K_eff selected
+        // keys are >= pf, so pf bounds the request's K_eff-th best
+        // candidate from below.  (One LDS histogram pass per 8-bit digit;
+        // measured much cheaper than a bit-by-bit ballot search of each
+        // wave's share, and exact, so fewer candidates survive the cut.)
+        uint64_t kmax = 0, kmin = ~0ull;
+        visit([&](uint64_t key) {
+            kmax = key > kmax ? key : kmax;
+            kmin = key < kmin ? key : kmin;
+        });
+        block_minmax<NT>(kmax, kmin, red64a);
+        uint64_t pf, mk;
+        radix_kth<NT>(K_eff, kmax, kmin, visit, hist3, hb, pf, mk);
+        tau = pf;
     }
     tau = tau > 1 ? tau : 1;                        // every real key is >= 1; 0 pads
 
