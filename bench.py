@@ -660,6 +660,66 @@ def cpu_baseline(inp: I.Inputs, min_seconds: float = 10.0):
                       f"of the same workload, {dt:.1f} s wall on {n} threads"}
 
 
+def measured_peaks(reps: int = 5):
+    """Sustained rates of this GPU from the probe kernels of libgr_peaks.so:
+    bf16 MFMA TFLOP/s (independent 32x32x16 chains), streaming copy and read
+    GB/s over 1 GiB buffers, and fp32 exp2 results per second.  Each figure
+    is the best of `reps` timed launches (HIP events on the launch stream).
+    They are reported beside the vendor peaks; the roofline fractions use
+    the vendor peaks."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "shared_prefix_beam_amd", "libgr_peaks.so"))
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.gr_peak_mfma.argtypes = [P, I32, I32, P]
+    lib.gr_peak_exp2.argtypes = [P, I32, I32, P]
+    lib.gr_peak_copy.argtypes = [P, P, I64, I32, P]
+    lib.gr_peak_read.argtypes = [P, I64, P, I32, P]
+    for f in (lib.gr_peak_mfma, lib.gr_peak_exp2, lib.gr_peak_copy, lib.gr_peak_read):
+        f.restype = ctypes.c_int
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+    grid = 2048                                    # 8 workgroups of 4 waves per compute unit
+    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    n_bytes = 1 << 30
+    src = torch.empty(n_bytes, dtype=torch.uint8, device="cuda").fill_(3)
+    dst = torch.empty_like(src)
+
+    def best_ms(call):
+        call()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            st = call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if st != 0:
+                raise RuntimeError(f"probe launch failed ({st})")
+            t = e0.elapsed_time(e1)
+            best = t if best is None else min(best, t)
+        return best
+
+    iters_m, iters_e = 2000, 4000
+    t_m = best_ms(lambda: lib.gr_peak_mfma(out.data_ptr(), grid, iters_m, h))
+    t_e = best_ms(lambda: lib.gr_peak_exp2(out.data_ptr(), grid, iters_e, h))
+    t_c = best_ms(lambda: lib.gr_peak_copy(src.data_ptr(), dst.data_ptr(), n_bytes // 16, grid, h))
+    t_r = best_ms(lambda: lib.gr_peak_read(src.data_ptr(), n_bytes // 16, out.data_ptr(), grid, h))
+    waves = grid * 4
+    mfma_flops = waves * iters_m * 4 * 32768.0
+    exps = grid * 256 * iters_e * 8.0
+    res = {"bf16_mfma_TFLOPs": mfma_flops / (t_m * 1e-3) / 1e12,
+           "hbm_copy_GBps": 2 * n_bytes / (t_c * 1e-3) / 1e9,
+           "hbm_read_GBps": n_bytes / (t_r * 1e-3) / 1e9,
+           "exp2_per_s": exps / (t_e * 1e-3),
+           "note": "best of %d launches; vendor peaks (%.0f TFLOP/s bf16, %.0f GB/s HBM) "
+                   "stay the roofline denominators" % (reps, PEAK_BF16_TFLOPS, PEAK_HBM_GBS)}
+    del src, dst
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -671,6 +731,8 @@ def main():
                     help="time one workload only and print its launch time (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run 10 device copies of 256 MiB (reference for HBM byte counters)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="print only the measured sustained MFMA, HBM and exp2 rates")
     ap.add_argument("--write-profiles", metavar="DIR",
                     help="summarise rocprofv3 outputs under DIR into profiles/ (no GPU needed)")
     args = ap.parse_args()
@@ -695,6 +757,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": 256 << 20, "launches": 10}), flush=True)
+        return
+    if args.peaks:
+        print(json.dumps(measured_peaks()), flush=True)
         return
     if args.only in ("select", "trie"):
         r = (measure_select(TRIE_CFGS[0], args.steps, args.warmup, trie=True)
@@ -772,6 +837,7 @@ def main():
                       "vs_dense_launch": dense["launch_ms"] / r["launch_ms"],
                       "spot_check": {"max_abs": r["spot_abs"], "lse_abs": r["spot_lse"]}})
     line["paged"] = paged
+    line["measured_peaks"] = measured_peaks()
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line), flush=True)

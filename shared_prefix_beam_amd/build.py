@@ -18,6 +18,9 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgr_attn.so")
 SOURCES = [os.path.join(CSRC, "gr_attn_kernels.hip"), os.path.join(CSRC, "gr_beam_step.hip"),
            os.path.join(CSRC, "gr_beam_select.hip"), os.path.join(CSRC, "gr_attn_api.cpp")]
+# measurement probes (sustained matrix, HBM and exp2 rates), a library of their own
+PEAKS_LIB = os.path.join(PKG, "libgr_peaks.so")
+PEAKS_SOURCES = [os.path.join(CSRC, "gr_peaks.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -26,9 +29,14 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source into libgr_attn.so (always recompiles)."""
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [HIPCC] + FLAGS + SOURCES + ["-o", tmp]
+    """Compile libgr_attn.so and the probe library libgr_peaks.so (always recompiles)."""
+    _build_one(PEAKS_SOURCES, PEAKS_LIB, verbose)
+    return _build_one(SOURCES, LIB, verbose)
+
+
+def _build_one(sources, lib, verbose):
+    tmp = lib + f".tmp{os.getpid()}"
+    cmd = [HIPCC] + FLAGS + sources + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -40,8 +48,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
