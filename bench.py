@@ -344,9 +344,27 @@ def write_select_profile(d, f_fetch, f_write, w="select"):
     print(f"wrote profiles/{name}.txt", flush=True)
 
 
-def measure(cfg: int, steps: int, warmup: int, page_size=None):
+def spot_rows(inp: I.Inputs):
+    """Rows checked against the oracle after timing: the first, middle and
+    last row of every request that has rows."""
+    rows = set()
+    for b in range(inp.B):
+        r0, r1 = int(inp.row_offset[b]), int(inp.row_offset[b + 1])
+        if r1 > r0:
+            rows.update((r0, (r0 + r1) // 2, r1 - 1))
+    return sorted(rows)
+
+
+def measure(cfg: int, steps: int, warmup: int, page_size=None, reps: int = 5,
+            latency_calls: int = 20):
     """Time gr_decode_attn on workload `cfg` (gr_decode_attn_paged with the
-    context scattered over pages of `page_size` tokens when it is given)."""
+    context scattered over pages of `page_size` tokens when it is given).
+
+    The timed region is `steps` back-to-back calls between two HIP events on
+    the launch stream (rep 0: ms_per_step and the launch time of the bench
+    line); `reps`-1 more such regions give the median and minimum.  Then
+    `latency_calls` single calls, each after a 512 MB write that evicts the
+    caches, with an event pair each, give the cold per-call latency."""
     import torch
     from shared_prefix_beam_amd import gr_attn
 
@@ -367,6 +385,14 @@ def measure(cfg: int, steps: int, warmup: int, page_size=None):
     W_max = int(max(inp.wl.W))
     stream = torch.cuda.current_stream()
 
+    # one workspace (zeroed once) serves every call: the calls run in order
+    # on one stream, and each leaves the split counters at zero
+    dims = gr_attn.Dims(B=inp.B, R=inp.R, Hq=inp.wl.Hq, Hkv=inp.wl.Hkv, D=inp.wl.D,
+                        W_max=W_max, T_cap=inp.T_cap, reserved=0, ctx_cap=inp.ctx_cap,
+                        beam_cap=inp.beam_cap, scale=0.0, flags=0)
+    workspace = gr_attn.attach_workspace(dims, None, "cuda")
+    ws_bytes = int(dims.workspace_bytes)
+
     # one front-end call per input copy validates shapes; the timed loop then
     # calls the C entry point directly with the same arguments
     if page_size:
@@ -374,10 +400,8 @@ def measure(cfg: int, steps: int, warmup: int, page_size=None):
             gr_attn.decode_attn_paged(s["q"], s["ctx_k"], s["ctx_v"], s["page_table"], page_size,
                                       s["ctx_len"], s["beam_k"], s["beam_v"], s["beam_path"],
                                       s["beam_len"], s["row_offset"], W_max=W_max,
-                                      ctx_cap=inp.ctx_cap, out=o, lse=l, stream=stream)
-        dims = gr_attn.Dims(B=inp.B, R=inp.R, Hq=inp.wl.Hq, Hkv=inp.wl.Hkv, D=inp.wl.D,
-                            W_max=W_max, T_cap=inp.T_cap, reserved=0, ctx_cap=inp.ctx_cap,
-                            beam_cap=inp.beam_cap, scale=0.0, flags=0)
+                                      ctx_cap=inp.ctx_cap, out=o, lse=l, stream=stream,
+                                      workspace=workspace)
         ctxs = [gr_attn.PagedCtx(k_pages=s["ctx_k"].data_ptr(), v_pages=s["ctx_v"].data_ptr(),
                                  page_table=s["page_table"].data_ptr(), page_size=page_size,
                                  pages_per_req=s["page_table"].shape[1],
@@ -389,9 +413,7 @@ def measure(cfg: int, steps: int, warmup: int, page_size=None):
         for s, (o, l) in zip(sets, outs):
             gr_attn.decode_attn(s["q"], s["ctx_k"], s["ctx_v"], s["ctx_len"], s["beam_k"],
                                 s["beam_v"], s["beam_path"], s["beam_len"], s["row_offset"],
-                                W_max=W_max, out=o, lse=l, stream=stream)
-        dims = gr_attn.make_dims(base["q"], base["ctx_k"], base["beam_k"], base["beam_path"],
-                                 W_max)
+                                W_max=W_max, out=o, lse=l, stream=stream, workspace=workspace)
         args = [tuple(t.data_ptr() for t in (s["row_offset"], s["q"], s["ctx_k"], s["ctx_v"],
                                              s["ctx_len"], s["beam_k"], s["beam_v"],
                                              s["beam_path"], s["beam_len"], o, l))
@@ -413,32 +435,81 @@ def measure(cfg: int, steps: int, warmup: int, page_size=None):
     # events recorded on the launch stream; the average launch duration is
     # their elapsed time / K, so the rate and the kernel duration come from
     # the same run.  No per-launch events, so the host never starves the GPU.
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(steps):
+    launch = []
+    ms_per_step = None
+    for rep in range(max(1, reps)):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(steps):
+            step(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        if rep == 0:
+            ms_per_step = wall * 1e3 / steps
+        launch.append(ev0.elapsed_time(ev1) / steps)
+
+    # cold per-call latency: a 512 MB write between calls evicts L2 and MALL
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    lat = []
+    for i in range(latency_calls):
+        flush.fill_(i & 255)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
         step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / steps
-    launch_ms = ev0.elapsed_time(ev1) / steps
+        e1.record(stream)
+        torch.cuda.synchronize()
+        lat.append(e0.elapsed_time(e1))
+    del flush
 
     # spot check of a few rows against the oracle (not timed)
     from oracle import oracle as O
-    rows = sorted({0, inp.R // 2, inp.R - 1})
+    rows = spot_rows(inp)
     out, lse = outs[0]
     step(0)
     torch.cuda.synchronize()
     ref_o, ref_l = O.decode_attn_inputs(inp, rows=rows)
     got_o = out.float().cpu().numpy()[rows]
     spot = float(np.abs(got_o - ref_o).max())
-    spot_lse = float(np.abs(lse.cpu().numpy()[rows] - ref_l).max())
+    fin = np.isfinite(ref_l)
+    got_l = lse.cpu().numpy()[rows]
+    spot_lse = float(np.abs(got_l[fin] - ref_l[fin]).max()) if fin.any() else 0.0
 
+    srt = sorted(launch)
     return dict(inp=inp, nbytes=nbytes, flops=flops, ms_per_step=ms_per_step,
-                launch_ms=launch_ms, n_sets=n_sets, spot_abs=spot, spot_lse=spot_lse)
+                launch_ms=launch[0], launch_median_ms=srt[len(srt) // 2], launch_min_ms=srt[0],
+                launch_reps_ms=launch, latency_ms=sorted(lat)[len(lat) // 2],
+                n_sets=n_sets, spot_abs=spot, spot_lse=spot_lse, spot_rows=len(rows),
+                workspace_bytes=ws_bytes)
+
+
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop per byte
+
+
+def config_entry(cfg: int, r) -> dict:
+    """One workload's numbers: rates at the median launch time of the
+    repetitions, both roofline fractions and which one bounds it."""
+    inp = r["inp"]
+    t = r["launch_median_ms"] * 1e-3
+    gbs = r["nbytes"] / t / 1e9
+    tf = r["flops"] / t / 1e12
+    ai = r["flops"] / r["nbytes"]
+    return {"config": cfg, "workload": inp.wl.name, "rows": inp.R, "heads": inp.wl.Hq,
+            "launch_us": r["launch_ms"] * 1e3, "launch_us_median": r["launch_median_ms"] * 1e3,
+            "launch_us_min": r["launch_min_ms"] * 1e3,
+            "launch_us_reps": [round(x * 1e3, 3) for x in r["launch_reps_ms"]],
+            "latency_us_cold": r["latency_ms"] * 1e3,
+            "beam_rows_per_s": inp.R / t, "hbm_GBps": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
+            "TFLOPs": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS,
+            "bound": "hbm" if ai < RIDGE else "mfma", "flop_per_byte": ai,
+            "algorithmic_bytes": r["nbytes"], "algorithmic_flops": r["flops"],
+            "workspace_bytes": r["workspace_bytes"],
+            "spot_check": {"rows": r["spot_rows"], "max_abs": r["spot_abs"],
+                           "lse_abs": r["spot_lse"]}}
 
 
 def measure_step(cfg: int, steps: int, warmup: int):
@@ -646,6 +717,14 @@ def cpu_baseline(inp: I.Inputs, min_seconds: float = 10.0):
     the workload until about `min_seconds` of wall time have been spent."""
     from oracle import oracle as O
     n = O.default_threads()
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     rows = np.arange(inp.R)
     passes = 0
     t0 = time.perf_counter()
@@ -657,7 +736,10 @@ def cpu_baseline(inp: I.Inputs, min_seconds: float = 10.0):
             break
     return {"value": passes * inp.R / dt, "unit": "beam-rows/s", "cores": n, "kind": "oracle",
             "sample": f"fp64 oracle, {passes} passes over all {inp.R} rows x {inp.wl.Hq} heads "
-                      f"of the same workload, {dt:.1f} s wall on {n} threads"}
+                      f"of the same workload, {dt:.1f} s wall on {n} threads",
+            "cpu_model": model, "host_cpus_visible": os.cpu_count(),
+            "threads_note": "all CPUs of the process affinity, capped by OMP_NUM_THREADS "
+                            "when set (the machine's allotment per GPU job)"}
 
 
 def measured_peaks(reps: int = 5):
@@ -727,7 +809,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--only", choices=["primary", "secondary", "beam_step", "select", "trie"],
+    ap.add_argument("--only", choices=["primary", "secondary", "cfg1", "cfg2", "cfg3", "cfg4",
+                                       "cfg5", "beam_step", "select", "trie"],
                     help="time one workload only and print its launch time (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run 10 device copies of 256 MiB (reference for HBM byte counters)")
@@ -773,7 +856,9 @@ def main():
                           "bit_exact": r["bit_exact"]}), flush=True)
         return
     if args.only:
-        r = measure(PRIMARY if args.only == "primary" else SECONDARY, args.steps, args.warmup)
+        cfg = {"primary": PRIMARY, "secondary": SECONDARY}.get(args.only)
+        cfg = cfg if cfg is not None else int(args.only[3:])
+        r = measure(cfg, args.steps, args.warmup, reps=1, latency_calls=0)
         print(json.dumps({"workload": r["inp"].wl.name, "launch_us": r["launch_ms"] * 1e3,
                           "ms_per_step": r["ms_per_step"]}), flush=True)
         return
@@ -802,6 +887,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel": "fused_decode_attn", "launch_us": prim["launch_ms"] * 1e3,
+                     "launch_us_median": prim["launch_median_ms"] * 1e3,
+                     "launch_us_min": prim["launch_min_ms"] * 1e3,
                      "algorithmic_bytes": prim["nbytes"]},
         "spot_check": {"max_abs": prim["spot_abs"], "lse_abs": prim["spot_lse"]},
     }
@@ -816,10 +903,22 @@ def main():
             "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
                          "traffic": recorded_traffic(si.wl.name),
-                         "launch_us": sec["launch_ms"] * 1e3, "algorithmic_flops": sec["flops"],
+                         "launch_us": sec["launch_ms"] * 1e3,
+                         "launch_us_median": sec["launch_median_ms"] * 1e3,
+                         "launch_us_min": sec["launch_min_ms"] * 1e3,
+                         "algorithmic_flops": sec["flops"],
                          "hbm_GBps": sec["nbytes"] / (sec["launch_ms"] * 1e-3) / 1e9},
             "spot_check": {"max_abs": sec["spot_abs"], "lse_abs": sec["spot_lse"]},
         }
+    # every workload of the set, the two above included: rates at the median
+    # of the repetitions, both roofline fractions, cold latency, spot check
+    runs = {PRIMARY: prim}
+    if sec is not None:
+        runs[SECONDARY] = sec
+    for c in sorted(I.WORKLOADS):
+        if c not in runs:
+            runs[c] = measure(c, args.steps, args.warmup)
+    line["configs"] = [config_entry(c, runs[c]) for c in sorted(runs)]
     line["beam_step"] = [step_entry(measure_step(c, args.steps, args.warmup)) for c in STEP_CFGS]
     line["beam_select"] = [select_entry(measure_select(c, args.steps, args.warmup))
                            for c in SELECT_CFGS]

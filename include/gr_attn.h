@@ -32,17 +32,20 @@
  *
  * Ownership and threading: the caller owns every buffer (device memory,
  * except the dims struct, which is host memory and is read during the call
- * only).  A call only enqueues work on `stream` (a hipStream_t; NULL = the
- * null stream) and returns; it never allocates, frees, copies between host
- * and device, synchronises, or reads device memory from the host, so it may
- * be captured into a HIP graph.  The library keeps no mutable global state:
+ * only), including the workspace (see gr_decode_attn_workspace_bytes).  A
+ * call only enqueues work on `stream` (a hipStream_t; NULL = the null stream)
+ * and returns; it never allocates, frees, copies between host and device,
+ * synchronises, or reads device memory from the host, so it may be captured
+ * into a HIP graph.  The library keeps no mutable global state:
  * concurrent calls on different streams are safe as long as their out/lse
  * buffers differ.  out and lse must not alias any input.
  *
  * Errors: every entry point returns GR_OK (0) or a negative GR_ERR_* code and
  * then has enqueued nothing, except GR_ERR_LAUNCH, which reports a failed
- * kernel launch.  Device-resident metadata (ctx_len, beam_len, row_offset,
- * beam_path) is not read by the host: its bounds above are preconditions.
+ * kernel launch.  GR_ERR_WORKSPACE: the dims' workspace is NULL, smaller than
+ * gr_decode_attn_workspace_bytes(dims) or not 256-byte aligned.
+ * Device-resident metadata (ctx_len, beam_len, row_offset, beam_path) is not
+ * read by the host: its bounds above are preconditions.
  * gr_check_metadata() verifies them on the device when a caller cannot
  * guarantee them.
  */
@@ -63,7 +66,8 @@ enum {
     GR_ERR_UNSUPPORTED = -3, /* D not 64/128, G > 8, no gfx950 device, ... */
     GR_ERR_ALIGN = -4,       /* a bf16 tensor pointer is not 16-byte aligned */
     GR_ERR_LAUNCH = -5,      /* the HIP runtime rejected a kernel launch */
-    GR_ERR_DEVICE = -6       /* a HIP runtime query failed */
+    GR_ERR_DEVICE = -6,      /* a HIP runtime query failed */
+    GR_ERR_WORKSPACE = -7    /* workspace NULL, too small or not 256-byte aligned */
 };
 
 /* Sizes of one call.  Host memory; read only during the call. */
@@ -79,15 +83,55 @@ typedef struct gr_decode_attn_dims {
     int64_t ctx_cap;  /* ContextKV tokens per request in ctx_k / ctx_v */
     int64_t beam_cap; /* BeamKV tokens per request in beam_k / beam_v */
     float scale;      /* softmax scale applied to q.k; 0 selects 1/sqrt(D) */
-    int32_t flags;    /* must be 0 */
+    int32_t flags;    /* 0 (the library plans the work), or GR_TILING(...) */
+    void *workspace;  /* DEVICE scratch owned by the caller (see below); may be
+                         NULL when gr_decode_attn_workspace_bytes() is 0 */
+    uint64_t workspace_bytes; /* size of `workspace` in bytes */
 } gr_decode_attn_dims;
+
+/*
+ * Per-call choice of the work decomposition, for tuning and tests (dims
+ * flags; 0 lets the library choose): workgroups of nqt query waves (32
+ * stacked query rows each) by nks key streams, with each (request, KV head,
+ * query tile) unit's context split over n_split workgroups.  nqt, nks in
+ * 1 .. 255, n_split in 1 .. 8; a tiling the library does not compile, or
+ * whose LDS does not fit, gives GR_ERR_UNSUPPORTED.  The result is the same
+ * (up to rounding order) for every tiling.
+ */
+#define GR_FLAG_TILING 0x40000000
+#define GR_TILING(nqt, nks, n_split) \
+    ((int32_t)(GR_FLAG_TILING | (nqt) | ((nks) << 8) | ((n_split) << 16)))
+
+/*
+ * Workspace gr_decode_attn / gr_decode_attn_paged need for these sizes, in
+ * bytes (0 when the call is planned without a cross-workgroup context split).
+ * The pages split the long ContextKV over several workers (Split-KV:
+ * GR-Inference blog, section on kernel design); when the (request, KV head)
+ * pairs alone cannot fill the GPU, the library splits each pair's context
+ * over several workgroups, which leave fp32 partial results (unnormalised
+ * output, running maximum and sums) in the workspace, and the last of them to
+ * finish combines them by log-sum-exp.  Layout: arrival counters first, then
+ * the partials; it is private to the library.
+ *
+ * Contract: the caller allocates at least this many bytes, 256-byte aligned,
+ * and ZERO-FILLS it once before its first use (the counters must start at
+ * zero; every completed call leaves them at zero again, so later calls,
+ * including graph replays, need no clearing).  One workspace must not be used
+ * by two calls that can run at the same time.  The size depends only on
+ * the dims (and on the GR_ATTN_TILE tuning override, read once per process).
+ * Returns 0 for a NULL or invalid dims.
+ */
+size_t gr_decode_attn_workspace_bytes(const gr_decode_attn_dims *dims);
 
 /*
  * Large-beam decode attention (shared ContextKV stage on bf16 MFMA with an
  * online softmax, per-beam BeamPath gather, log-sum-exp merge), one launch
- * on `stream`.  row_offset is a DEVICE pointer to int32[B+1].
+ * on `stream`.  row_offset is a DEVICE pointer to int32[B+1]; it is a
+ * positional argument (not a dims field) because it is device memory that a
+ * decode loop updates every step, while the dims struct holds host values.
  * The ContextKV of each (request, KV head) is read from HBM once per call
- * rather than once per beam.
+ * rather than once per beam.  dims->workspace must hold
+ * gr_decode_attn_workspace_bytes(dims) bytes (see there).
  */
 int gr_decode_attn(const gr_decode_attn_dims *dims, const int32_t *row_offset,
                    const void *q, const void *ctx_k, const void *ctx_v,
@@ -101,7 +145,8 @@ int gr_decode_attn(const gr_decode_attn_dims *dims, const int32_t *row_offset,
  * ContextKV (SID-GR README, section "Performance Breakdown": the
  * general path treats B x W beams as independent decode rows).  Same
  * arguments, layouts and results; kept as an in-library comparator.
- * Requires ctx_cap + T_cap <= 16384.
+ * Requires ctx_cap + T_cap <= 16384; needs no workspace (the dims' workspace
+ * fields are ignored).
  */
 int gr_decode_attn_generic(const gr_decode_attn_dims *dims, const int32_t *row_offset,
                            const void *q, const void *ctx_k, const void *ctx_v,

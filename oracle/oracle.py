@@ -41,12 +41,16 @@ def build(force: bool = False) -> str:
 
 
 def default_threads() -> int:
-    """Host threads for the oracle: the CPUs this process may run on, at most 16."""
+    """Host threads for the oracle: every CPU this process may run on, or
+    fewer when OMP_NUM_THREADS allots fewer (a machine's share for one job)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
         n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
 
 
 def _open(path: str):

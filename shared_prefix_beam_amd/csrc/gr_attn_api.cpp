@@ -46,8 +46,14 @@ int validate(const gr_decode_attn_dims *d)
     if (!d)
         return GR_ERR_NULL;
     if (d->B < 0 || d->R < 0 || d->Hq <= 0 || d->Hkv <= 0 || d->W_max < 0 || d->T_cap < 0 ||
-        d->ctx_cap < 0 || d->beam_cap < 0 || d->reserved != 0 || d->flags != 0)
+        d->ctx_cap < 0 || d->beam_cap < 0 || d->reserved != 0)
         return GR_ERR_DIMS;
+    if (d->flags != 0) {
+        const int nqt = d->flags & 255, nks = (d->flags >> 8) & 255, sp = (d->flags >> 16) & 255;
+        if ((d->flags & ~(GR_FLAG_TILING | 0xffffff)) != 0 || !(d->flags & GR_FLAG_TILING) ||
+            nqt < 1 || nks < 1 || sp < 1 || sp > 8)
+            return GR_ERR_DIMS;
+    }
     if (d->Hq % d->Hkv != 0)
         return GR_ERR_DIMS;
     if (!(d->scale >= 0.f) || std::isinf(d->scale))
@@ -115,59 +121,155 @@ gr::Params make_params(const gr_decode_attn_dims *d, const int32_t *row_offset, 
 }
 
 // Work decomposition.  A workgroup covers 32*NQT stacked query rows of one
-// (request, KV head) pair (a wave owns 32 rows) and splits that pair's
-// context over NKS key streams.  Wide query tiles share each K/V tile in LDS
-// between more waves; more key streams keep the grid large when the stacks
-// are short.  Candidates are tried in order of preference and the first one
-// whose grid fills at least 7/8 of two waves per SIMD is taken; else the
-// last one that fits.  (4,1) comes first: two of its
-// workgroups share a compute unit, and as their barriers are independent the
-// two waves of a SIMD drift out of phase, so one's softmax overlaps the
-// other's matrix work (measured: 78 us against 96 us for (8,1) at 4 requests
-// x 900 beams x 2048 context tokens).
+// (request, KV head) pair (a wave owns 32 rows) and splits its share of that
+// pair's context over NKS key streams.  Wide query tiles share each K/V tile
+// in LDS between more waves; more key streams keep the grid large when the
+// stacks are short.  (4,1) is preferred: two of its workgroups share a
+// compute unit, and as their barriers are independent the two waves of a
+// SIMD drift out of phase, so one's softmax overlaps the other's matrix work
+// (measured: 78 us against 96 us for (8,1) at 4 requests x 900 beams x 2048
+// context tokens).  When its grid cannot fill the GPU (few pairs, short
+// stacks), the context of each (pair, query tile) is split over n_split
+// workgroups that combine their partials through the workspace; only when
+// the context is too short for that do wider key streams take over.
 struct Plan {
-    int nqt, nks, n_qt, grid;
+    int nqt, nks, n_split, n_qt, grid;
 };
 
 constexpr int kSIMDs = 256 * 4;
 constexpr int kLdsBytes = 160 * 1024;     // LDS per compute unit
 // The fused kernel's own static LDS (the block-wide vote of its re-sweep
-// check); the dynamic segment, aligned to 1 KB, starts after it.
+// check and the split-arrival flag); the dynamic segment, aligned to 1 KB,
+// starts after it.
 constexpr int kStaticLds = 1024;
+constexpr int kMaxSplit = 8;              // workgroups per (pair, query tile)
+constexpr int kMinSplitTiles = 4;         // 32-key tiles each split sweeps, at least
+constexpr int kKeyTile = 32;
+
+bool tiling_fits(int D, int nqt, int nks)
+{
+    const int lds = gr::fused_lds_bytes(D, nqt, nks);
+    return lds > 0 && lds + kStaticLds <= kLdsBytes;
+}
+
+// "NQT,NKS[,SPLIT]" from GR_ATTN_TILE (tuning and tests), read once per
+// process; a tiling that is not compiled or does not fit the LDS is ignored.
+struct TileOverride {
+    int nqt = 0, nks = 0, split = 0;
+};
+const TileOverride &tile_override()
+{
+    static const TileOverride o = [] {
+        TileOverride t;
+        const char *env = std::getenv("GR_ATTN_TILE");
+        int a = 0, b = 0, c = 0;
+        const int n = env ? std::sscanf(env, "%d,%d,%d", &a, &b, &c) : 0;
+        if (n >= 2 && a > 0 && b > 0) {
+            t.nqt = a;
+            t.nks = b;
+            t.split = n >= 3 && c > 0 ? (c < kMaxSplit ? c : kMaxSplit) : 1;
+        }
+        return t;
+    }();
+    return o;
+}
 
 Plan plan(const gr_decode_attn_dims *d)
 {
     const int G = d->Hq / d->Hkv;
     const int64_t M = static_cast<int64_t>(d->W_max) * G;
     const int64_t pairs = static_cast<int64_t>(d->B) * d->Hkv;
-    static const int cand[][2] = {{4, 1}, {8, 1}, {4, 2}, {2, 2}, {2, 4}};
-    Plan best{1, 4, 0, 0};
-    const char *env = std::getenv("GR_ATTN_TILE");     // "NQT,NKS", tuning only
-    int fq = 0, fk = 0;
-    if (env && std::sscanf(env, "%d,%d", &fq, &fk) == 2 && gr::fused_lds_bytes(d->D, fq, fk) > 0) {
-        best.nqt = fq;
-        best.nks = fk;
+    const int64_t n_tiles = (d->ctx_cap + kKeyTile - 1) / kKeyTile;
+    const int64_t want = 7 * 2 * kSIMDs / 8;   // 7/8 of two waves per SIMD
+    auto waves = [&](int nqt, int nks) {
+        return pairs * ((M + 32 * nqt - 1) / (32 * nqt)) * nqt * nks;
+    };
+    Plan best{1, 4, 1, 0, 0};
+    const TileOverride &o = tile_override();
+    if (d->flags & GR_FLAG_TILING) {
+        best.nqt = d->flags & 255;
+        best.nks = (d->flags >> 8) & 255;
+        best.n_split = (d->flags >> 16) & 255;
+        if (!tiling_fits(d->D, best.nqt, best.nks))
+            best.grid = -2;                     // not compiled or too large
+    } else if (o.nqt > 0 && tiling_fits(d->D, o.nqt, o.nks)) {
+        best.nqt = o.nqt;
+        best.nks = o.nks;
+        best.n_split = o.split;
     } else {
+        static const int cand[][2] = {{4, 1}, {8, 1}, {4, 2}, {2, 2}, {2, 4}};
+        bool chosen = false;
+        if (tiling_fits(d->D, 4, 1)) {
+            const int64_t w = waves(4, 1);
+            int s = 1;
+            while (w * s < want && 2 * s <= kMaxSplit && n_tiles >= 2 * s * kMinSplitTiles)
+                s *= 2;
+            if (w * s >= want || s > 1) {
+                best = Plan{4, 1, s, 0, 0};
+                chosen = true;
+            }
+        }
         for (const auto &c : cand) {
-            const int lds = gr::fused_lds_bytes(d->D, c[0], c[1]);
-            if (lds <= 0 || lds + kStaticLds > kLdsBytes)
+            if (chosen)
+                break;
+            if (!tiling_fits(d->D, c[0], c[1]))
                 continue;
-            const int64_t n_qt = (M + 32 * c[0] - 1) / (32 * c[0]);
             best.nqt = c[0];
             best.nks = c[1];
-            if (pairs * n_qt * c[0] * c[1] * 8 >= 7 * 2 * kSIMDs)
+            best.n_split = 1;
+            if (waves(c[0], c[1]) >= want)
                 break;
         }
     }
+    if (best.grid == -2)
+        return best;
     best.n_qt = static_cast<int>((M + 32 * best.nqt - 1) / (32 * best.nqt));
     const int64_t pairs_per_xcd = (pairs + 7) / 8;
-    best.grid = static_cast<int>(8 * pairs_per_xcd * best.n_qt);
+    const int64_t grid = 8 * pairs_per_xcd * best.n_qt * best.n_split;
+    best.grid = grid > INT32_MAX ? -1 : static_cast<int>(grid);
     return best;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+// Workspace layout of a plan: arrival counters, then the wave partials.
+size_t workspace_bytes(const gr_decode_attn_dims *d, const Plan &pl)
+{
+    if (pl.n_split <= 1 || pl.grid <= 0)
+        return 0;
+    const size_t units = static_cast<size_t>(d->B) * d->Hkv * pl.n_qt;
+    return align256(units * sizeof(int32_t)) +
+           units * pl.n_split * pl.nqt * static_cast<size_t>(gr::fused_part_bytes(d->D));
+}
+
+// Checks the dims' workspace against the plan and points the kernel
+// parameters at it.
+int bind_workspace(const gr_decode_attn_dims *d, const Plan &pl, gr::Params &p)
+{
+    p.n_split = pl.n_split;
+    const size_t need = workspace_bytes(d, pl);
+    if (need == 0)
+        return GR_OK;
+    if (!d->workspace || d->workspace_bytes < need ||
+        (reinterpret_cast<uintptr_t>(d->workspace) & 255u))
+        return GR_ERR_WORKSPACE;
+    const size_t units = static_cast<size_t>(d->B) * d->Hkv * pl.n_qt;
+    char *w = static_cast<char *>(d->workspace);
+    p.ws_count = reinterpret_cast<int32_t *>(w);
+    p.ws_part = w + align256(units * sizeof(int32_t));
+    return GR_OK;
 }
 
 }  // namespace
 
 extern "C" {
+
+size_t gr_decode_attn_workspace_bytes(const gr_decode_attn_dims *d)
+{
+    if (validate(d) != GR_OK || d->R == 0 || d->B == 0 || d->W_max == 0)
+        return 0;
+    return workspace_bytes(d, plan(d));
+}
 
 int gr_decode_attn(const gr_decode_attn_dims *d, const int32_t *row_offset, const void *q,
                    const void *ctx_k, const void *ctx_v, const int32_t *ctx_len,
@@ -183,15 +285,20 @@ int gr_decode_attn(const gr_decode_attn_dims *d, const int32_t *row_offset, cons
         return st;
     if (d->R == 0 || d->B == 0 || d->W_max == 0)
         return GR_OK;
-    st = device_ok();
-    if (st != GR_OK)
-        return st;
     gr::Params p = make_params(d, row_offset, q, ctx_k, ctx_v, ctx_len, beam_k, beam_v,
                                beam_path, beam_len, out, lse);
     const Plan pl = plan(d);
+    if (pl.grid < 0)
+        return pl.grid == -2 ? GR_ERR_UNSUPPORTED : GR_ERR_DIMS;
     p.n_qt = pl.n_qt;
-    if (pl.grid <= 0)
+    st = bind_workspace(d, pl, p);
+    if (st != GR_OK)
+        return st;
+    if (pl.grid == 0)
         return GR_OK;
+    st = device_ok();
+    if (st != GR_OK)
+        return st;
     const hipError_t e =
         gr::launch_fused(p, pl.nqt, pl.nks, pl.grid, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GR_OK : GR_ERR_LAUNCH;
@@ -222,9 +329,6 @@ int gr_decode_attn_paged(const gr_decode_attn_dims *d, const gr_paged_ctx *c,
         return st;
     if (d->R == 0 || d->B == 0 || d->W_max == 0)
         return GR_OK;
-    st = device_ok();
-    if (st != GR_OK)
-        return st;
     gr::Params p = make_params(d, row_offset, q, c->k_pages, c->v_pages, ctx_len, beam_k, beam_v,
                                beam_path, beam_len, out, lse);
     p.page_table = c->page_table;
@@ -232,9 +336,17 @@ int gr_decode_attn_paged(const gr_decode_attn_dims *d, const gr_paged_ctx *c,
     p.pages_per_req = c->pages_per_req;
     p.n_pages = c->n_pages;
     const Plan pl = plan(d);
+    if (pl.grid < 0)
+        return pl.grid == -2 ? GR_ERR_UNSUPPORTED : GR_ERR_DIMS;
     p.n_qt = pl.n_qt;
-    if (pl.grid <= 0)
+    st = bind_workspace(d, pl, p);
+    if (st != GR_OK)
+        return st;
+    if (pl.grid == 0)
         return GR_OK;
+    st = device_ok();
+    if (st != GR_OK)
+        return st;
     const hipError_t e =
         gr::launch_fused(p, pl.nqt, pl.nks, pl.grid, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GR_OK : GR_ERR_LAUNCH;
@@ -496,10 +608,11 @@ const char *gr_status_str(int status)
     case GR_ERR_ALIGN: return "misaligned tensor pointer";
     case GR_ERR_LAUNCH: return "kernel launch failed";
     case GR_ERR_DEVICE: return "HIP device query failed";
+    case GR_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     default: return "unknown status";
     }
 }
 
-int gr_version(void) { return 100; }
+int gr_version(void) { return 200; }
 
 }  // extern "C"

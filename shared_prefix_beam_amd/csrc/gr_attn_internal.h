@@ -15,6 +15,14 @@ struct Params {
     int64_t ctx_cap, beam_cap;
     float scale_log2;   // softmax scale * log2(e)
     int n_qt;           // query tiles per (request, KV head) pair in the fused grid
+    // Cross-workgroup context split (fused kernel): the n_split workgroups of
+    // one (pair, query tile) unit each sweep 1/n_split of the context and
+    // leave fp32 partials in ws_part; the last to arrive (counted in
+    // ws_count[unit], which it resets to 0) combines them.  n_split == 1:
+    // no workspace is touched.
+    int n_split;
+    int32_t *ws_count;  // [pairs * n_qt] arrival counters, zero between calls
+    char *ws_part;      // [pairs * n_qt][n_split][NQT] wave partials of fused_part_bytes(D)
     // Paged ContextKV (fused kernel only): when page_table is set, ctx_k /
     // ctx_v are page pools [n_pages][page_size][Hkv][D] and token j of request
     // b is row j % page_size of page page_table[b * pages_per_req + j / page_size].
@@ -64,7 +72,14 @@ struct SelParams {
     int B, R_old, R_new, V, K_max;
 };
 // Workspace bytes of the six tables above (each 256-byte aligned).
-size_t beam_select_workspace(int R_old, int K_max);
+inline size_t beam_select_workspace(int R_old, int K_max)
+{
+    auto al = [](size_t n) { return (n + 255) & ~(size_t)255; };
+    const size_t R = static_cast<size_t>(R_old);
+    return al(R * SEL_LIST * sizeof(uint64_t)) + al(R * sizeof(float)) +
+           al(R * sizeof(int32_t)) + al(R * static_cast<size_t>(K_max) * sizeof(uint64_t)) +
+           2 * al(R * sizeof(int32_t));
+}
 
 // Longest key list the generic comparator keeps in LDS.
 constexpr int GENERIC_MAX_KEYS = 16320;
@@ -76,7 +91,38 @@ constexpr int GENERIC_MAX_KEYS = 16320;
     X(128, 8, 1, 4, 2) X(128, 4, 1, 4, 2) X(128, 4, 2, 4, 2) X(128, 2, 2, 4, 2)    \
     X(64, 4, 1, 4, 2) X(64, 2, 2, 4, 2) X(64, 2, 4, 3, 2)
 
-int fused_lds_bytes(int D, int nqt, int nks);
+// LDS of the fused kernel (host and device agree on it): the ring of NKS *
+// NBUF context tiles of FUSED_KT keys (K then V rows, D bf16 each), which the
+// beam gathers and the merge of the key streams reuse, then the staged
+// BeamPath entries.
+constexpr int FUSED_KT = 32;
+constexpr int FUSED_PTAB_BYTES = 4096;
+constexpr int fused_lds_main(int D, int nqt, int nks, int nbuf)
+{
+    const int tile = 2 * FUSED_KT * D * 2;
+    const int stage = nks * nbuf * tile;
+    const int oslot = 32 * (D + 4) * 4 + 32 * 16;  // one wave's O partial + (max, sums)
+    const int merge = (nks - 1) * nqt * oslot;
+    return stage > merge ? stage : merge;
+}
+constexpr int fused_lds_total(int D, int nqt, int nks, int nbuf)
+{
+    return fused_lds_main(D, nqt, nks, nbuf) + FUSED_PTAB_BYTES;
+}
+// Dynamic LDS of a compiled (D, NQT, NKS) instantiation, -1 if not compiled.
+inline int fused_lds_bytes(int D, int nqt, int nks)
+{
+#define GR_LDS_CASE(d, a, c, nb, oc)                                                  \
+    if (D == d && nqt == a && nks == c)                                               \
+        return fused_lds_total(d, a, c, nb);
+    GR_FOR_EACH_FUSED_CONFIG(GR_LDS_CASE)
+#undef GR_LDS_CASE
+    return -1;
+}
+// Bytes of one wave's partial result in the split workspace: the unnormalised
+// O^T fragments (D/2 floats per lane) and (max, sum, sum) per lane, in the
+// wave's own lane order (16-byte vectors, lane-contiguous).
+constexpr int fused_part_bytes(int D) { return (D / 8 + 1) * 64 * 16; }
 hipError_t launch_fused(const Params &p, int nqt, int nks, int grid, hipStream_t s);
 hipError_t launch_generic(const Params &p, hipStream_t s);
 hipError_t launch_check(const MetaCheck &c, hipStream_t s);

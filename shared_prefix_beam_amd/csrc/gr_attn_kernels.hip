@@ -38,6 +38,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "gr_attn_internal.h"
@@ -52,9 +53,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int KT = 32;          // keys per context tile
+constexpr int KT = FUSED_KT;    // keys per context tile
 constexpr int PSTEPS = 4;       // beam steps gathered into LDS at a time, at most
-constexpr int PTAB_BYTES = 4096;  // LDS for the BeamPath entries of a workgroup's beams
+constexpr int PTAB_BYTES = FUSED_PTAB_BYTES;  // LDS for the BeamPath entries of a workgroup's beams
 constexpr float SAFE_SUM = 1.8446744e19f;  // 2^64: largest row sum accepted in pass 0
 constexpr float NEG_INF = -__builtin_huge_valf();
 constexpr uint32_t BF16_ONES = 0x3f803f80u;  // two bf16 ones
@@ -88,6 +89,8 @@ constexpr int lds_main()
 {
     constexpr int stage = NKS * NBUF * Geo<D>::TILE;
     constexpr int merge = (NKS - 1) * NQT * Geo<D>::OSLOT;
+    static_assert((stage > merge ? stage : merge) == fused_lds_main(D, NQT, NKS, NBUF),
+                  "host and device LDS layouts differ");
     return stage > merge ? stage : merge;
 }
 template <int D, int NQT, int NKS, int NBUF>
@@ -201,11 +204,16 @@ void fused_decode_attn(const Params p)
     // Workgroups are dispatched round-robin over the 8 XCDs; all query tiles
     // of one (request, KV head) pair go to the same XCD so that its L2 holds
     // the pair's ContextKV for every tile.
+    // With a context split, the n_split workgroups of one (pair, query tile)
+    // unit have consecutive ids on the XCD, so they run together and their
+    // partials meet in that XCD's L2.
     const int bid = blockIdx.x;
     const int xcd = bid & 7;
     const int j = bid >> 3;
-    const int pair = (j / p.n_qt) * 8 + xcd;
-    const int qtile = j % p.n_qt;
+    const int per_pair = p.n_qt * p.n_split;
+    const int pair = (j / per_pair) * 8 + xcd;
+    const int qtile = (j % per_pair) / p.n_split;
+    const int split = j % p.n_split;
     if (pair >= p.B * p.Hkv)
         return;
     const int b = pair / p.Hkv;
@@ -225,6 +233,9 @@ void fused_decode_attn(const Params p)
     const int lane = tid & 63;
     const int qt = wave % NQT;
     const int ks = wave / NQT;
+    // global key stream: the unit's n_split * NKS streams share its context
+    const int gs = split * NKS + ks;
+    const int GS = p.n_split * NKS;
     const int h = lane >> 5;
     const int c32 = lane & 31;
     const int wrow0 = tile_row0 + qt * 32;        // first stacked row of this wave
@@ -294,9 +305,9 @@ void fused_decode_attn(const Params p)
 
     // ---- shared (context) stage -----------------------------------------
     const int n_tiles = (L + KT - 1) / KT;
-    const int t_begin = (ks * n_tiles) / NKS;
-    const int n_mine = ((ks + 1) * n_tiles) / NKS - t_begin;
-    const int iters = (n_tiles + NKS - 1) / NKS;  // same for every wave (barrier count)
+    const int t_begin = (gs * n_tiles) / GS;
+    const int n_mine = ((gs + 1) * n_tiles) / GS - t_begin;
+    const int iters = (n_tiles + GS - 1) / GS;    // same for every wave (barrier count)
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
     const uint32_t stream_off = ks * (NBUF * Gm::TILE);        // byte offset of this stream
     // dense: request b's slice; paged: the pools (pages are located per load)
@@ -747,7 +758,7 @@ void fused_decode_attn(const Params p)
         block_barrier();                           // buffers free for the next user
     };
 
-    // ---- per-beam stage: BeamKV steps ks, ks+NKS, ... along BeamPath ------
+    // ---- per-beam stage: BeamKV steps gs, gs+GS, ... along BeamPath ------
     // Each lane folds the K and V rows of its query's path token for a step
     // into its (max, sums, O) online.  When G divides 32 the 32/G beams of a
     // wave are gathered first into the (still unused) tile buffers with
@@ -756,11 +767,11 @@ void fused_decode_attn(const Params p)
     // row beta's 16-byte chunks sit at slot chunk ^ (beta & (CH-1)).  The
     // path entries come from the staged table (else from the lane beta*G,
     // which loads its own).  Otherwise each lane loads its rows from memory.
-    const int n_steps = T > ks ? (T - ks + NKS - 1) / NKS : 0;
+    const int n_steps = T > gs ? (T - gs + GS - 1) / GS : 0;
     auto step_idx = [&](int i) __attribute__((always_inline)) {
         int qr = qrow;
         asm volatile("" : "+v"(qr));
-        return qvalid ? p.beam_path[(int64_t)qr * p.T_cap + ks + i * NKS] : 0;
+        return qvalid ? p.beam_path[(int64_t)qr * p.T_cap + gs + i * GS] : 0;
     };
     auto fold = [&](const u32x4 (&kr)[Gm::DC], const u32x2 (&vr)[Gm::DB][4])
                     __attribute__((always_inline)) {
@@ -792,7 +803,10 @@ void fused_decode_attn(const Params p)
     const int nb = 32 / G;                         // beams of a wave (G divides 32)
     const int sb = 2 * nb * Gm::ROW;               // LDS bytes per gathered step
     const int fit = RING / (NQT * NKS * sb);
-    const int sch = (32 % G == 0) ? (fit < PSTEPS ? fit : PSTEPS) : 0;
+    // The LDS gather moves whole 1 KB loads of 1024/ROW rows, so it needs at
+    // least that many beams per wave (not so for D = 64 at G = 8: 4 beams of
+    // 128 bytes); other shapes take the per-lane gather.
+    const int sch = (32 % G == 0 && nb * Gm::ROW >= 1024) ? (fit < PSTEPS ? fit : PSTEPS) : 0;
     auto beam_stage = [&]() __attribute__((always_inline)) {
         if (wave_live && sch > 0) {
             const uint32_t area = lds0 + wave * sch * sb;
@@ -819,7 +833,7 @@ void fused_decode_attn(const Params p)
                         for (int u = 0; u < MAXL; ++u) {
                             const int beta = u * (1024 / Gm::ROW) + beta_l;
                             rid[i][u] = (i < cnt && u < lpr)
-                                            ? ptab_l[(tb_w + beta) * T + ks + (s0 + i) * NKS]
+                                            ? ptab_l[(tb_w + beta) * T + gs + (s0 + i) * GS]
                                             : 0;
                         }
                 } else {
@@ -984,6 +998,96 @@ void fused_decode_attn(const Params p)
         }
     }
 
+    // ---- context split: partials through the workspace --------------------
+    // Every workgroup of the unit leaves its waves' (O, max, sums) in the
+    // workspace in lane order, then counts itself in; the last to arrive
+    // resets the counter for the next call and combines all n_split partials
+    // in ascending split order (its own from registers), so the result does
+    // not depend on which workgroup finishes last.  The device-scope fences
+    // make the partials visible to that workgroup before its count returns.
+    if (p.n_split > 1) {
+        __shared__ int s_last;
+        const int unit = pair * p.n_qt + qtile;
+        constexpr int PB = fused_part_bytes(D);
+        constexpr int NV = D / 8;                  // f32x4 per lane of a wave's O^T
+        char *const part_u = p.ws_part + (size_t)unit * p.n_split * NQT * PB;
+        if (ks == 0 && wave_live) {
+            char *mine = part_u + ((size_t)split * NQT + qt) * PB + 16 * lane;
+            if (m_ref != NEG_INF) {                // nothing to add otherwise
+#pragma unroll
+                for (int db = 0; db < Gm::DB; ++db)
+#pragma unroll
+                    for (int rg = 0; rg < 4; ++rg)
+                        *reinterpret_cast<f32x4 *>(mine + (db * 4 + rg) * 1024) =
+                            f32x4{o[db][4 * rg], o[db][4 * rg + 1], o[db][4 * rg + 2],
+                                  o[db][4 * rg + 3]};
+            }
+            *reinterpret_cast<f32x4 *>(mine + NV * 1024) = f32x4{m_ref, l_run, l_lse, 0.f};
+        }
+        __threadfence();
+        __syncthreads();
+        if (tid == 0) {
+            const int last = atomicAdd(p.ws_count + unit, 1) == p.n_split - 1;
+            if (last)
+                p.ws_count[unit] = 0;              // next call starts from zero
+            s_last = last;
+        }
+        __syncthreads();
+        if (!s_last)
+            return;
+        __threadfence();
+        if (ks == 0 && wave_live) {
+            const float m_own = m_ref, lr_own = l_run, ll_own = l_lse;
+            float mm = NEG_INF, lr = 0.f, ll = 0.f;
+#pragma unroll
+            for (int db = 0; db < Gm::DB; ++db)
+                acc[db] = f32x16{};                // the combined O^T
+#pragma unroll 1
+            for (int sp = 0; sp < p.n_split; ++sp) {
+                const char *src = part_u + ((size_t)sp * NQT + qt) * PB + 16 * lane;
+                float ms = m_own, lrs = lr_own, lls = ll_own;
+                if (sp != split) {
+                    const f32x4 st = *reinterpret_cast<const f32x4 *>(src + NV * 1024);
+                    ms = st[0];
+                    lrs = st[1];
+                    lls = st[2];
+                }
+                if (ms == NEG_INF)
+                    continue;                      // an empty partial
+                const float mn = __builtin_fmaxf(mm, ms);
+                const float a = mm == NEG_INF ? 0.f : exp2_fast(mm - mn);
+                const float bw = exp2_fast(ms - mn);
+                if (sp == split) {
+#pragma unroll
+                    for (int db = 0; db < Gm::DB; ++db)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            acc[db][e] = acc[db][e] * a + o[db][e] * bw;
+                } else {
+#pragma unroll
+                    for (int db = 0; db < Gm::DB; ++db)
+#pragma unroll
+                        for (int rg = 0; rg < 4; ++rg) {
+                            const f32x4 v =
+                                *reinterpret_cast<const f32x4 *>(src + (db * 4 + rg) * 1024);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                acc[db][4 * rg + e] = acc[db][4 * rg + e] * a + v[e] * bw;
+                        }
+                }
+                mm = mn;
+                lr = lr * a + lrs * bw;
+                ll = ll * a + lls * bw;
+            }
+#pragma unroll
+            for (int db = 0; db < Gm::DB; ++db)
+                o[db] = acc[db];
+            m_ref = mm;
+            l_run = lr;
+            l_lse = ll;
+        }
+    }
+
     // ---- epilogue: normalise, bf16 output, fp32 natural-log LSE ----------
     if (ks == 0 && wave_live && qvalid) {
         // recomputed here from opaque copies: the 64-bit row offset of the Q
@@ -1126,22 +1230,22 @@ static hipError_t launch_fused_t(const Params &p, int grid, hipStream_t s)
 {
     constexpr int lds = lds_bytes<D, NQT, NKS, NBUF>();
     auto kern = fused_decode_attn<D, NQT, NKS, NBUF, OCC, PAGED>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    // the dynamic-LDS limit is raised once per instantiation and device
+    static std::atomic<uint64_t> attr_set{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
         return e;
+    const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+    if (!bit || !(attr_set.load(std::memory_order_acquire) & bit)) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess)
+            return e;
+        attr_set.fetch_or(bit, std::memory_order_release);
+    }
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NQT * NKS), lds, s, p);
     return hipGetLastError();
-}
-
-int fused_lds_bytes(int D, int nqt, int nks)
-{
-#define GR_LDS_CASE(d, a, c, nb, oc)                                                  \
-    if (D == d && nqt == a && nks == c)                                               \
-        return lds_bytes<d, a, c, nb>();
-    GR_FOR_EACH_FUSED_CONFIG(GR_LDS_CASE)
-#undef GR_LDS_CASE
-    return -1;
 }
 
 hipError_t launch_fused(const Params &p, int nqt, int nks, int grid, hipStream_t s)

@@ -1089,15 +1089,6 @@ __global__ __launch_bounds__(SEL_REQ_THREADS) void select_request(const SelParam
     }
 }
 
-size_t beam_select_workspace(int R_old, int K_max)
-{
-    auto al = [](size_t n) { return (n + 255) & ~(size_t)255; };
-    const size_t R = static_cast<size_t>(R_old);
-    return al(R * SEL_LIST * sizeof(uint64_t)) + al(R * sizeof(float)) +
-           al(R * sizeof(int32_t)) + al(R * static_cast<size_t>(K_max) * sizeof(uint64_t)) +
-           2 * al(R * sizeof(int32_t));
-}
-
 hipError_t launch_beam_select(const SelParams &p, hipStream_t s)
 {
     if (p.R_old > 0) {

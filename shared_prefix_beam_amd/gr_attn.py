@@ -24,8 +24,21 @@ GR_ERR_UNSUPPORTED = -3
 GR_ERR_ALIGN = -4
 GR_ERR_LAUNCH = -5
 GR_ERR_DEVICE = -6
+GR_ERR_WORKSPACE = -7
+GR_FLAG_TILING = 0x40000000
 
-EXPORTS = ("gr_decode_attn", "gr_decode_attn_generic", "gr_decode_attn_paged",
+
+def tiling_flags(tiling) -> int:
+    """dims flags for a forced (nqt, nks[, n_split]) work decomposition
+    (GR_TILING in include/gr_attn.h); None -> 0 (the library plans)."""
+    if tiling is None:
+        return 0
+    nqt, nks, *rest = tiling
+    split = rest[0] if rest else 1
+    return GR_FLAG_TILING | int(nqt) | (int(nks) << 8) | (int(split) << 16)
+
+EXPORTS = ("gr_decode_attn_workspace_bytes", "gr_decode_attn", "gr_decode_attn_generic",
+           "gr_decode_attn_paged",
            "gr_check_metadata", "gr_beam_step", "gr_beam_select_workspace_bytes",
            "gr_beam_select", "gr_beam_select_trie", "gr_status_str", "gr_version")
 
@@ -37,7 +50,8 @@ class Dims(ctypes.Structure):
                 ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32), ("W_max", ctypes.c_int32),
                 ("T_cap", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("ctx_cap", ctypes.c_int64), ("beam_cap", ctypes.c_int64),
-                ("scale", ctypes.c_float), ("flags", ctypes.c_int32)]
+                ("scale", ctypes.c_float), ("flags", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64)]
 
 
 class StepDims(ctypes.Structure):
@@ -97,6 +111,8 @@ def load() -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.argtypes = attn_args
             fn.restype = ctypes.c_int
+        lib.gr_decode_attn_workspace_bytes.argtypes = [DP]
+        lib.gr_decode_attn_workspace_bytes.restype = ctypes.c_size_t
         lib.gr_check_metadata.argtypes = [DP, P, P, P, P, P, P]
         lib.gr_check_metadata.restype = ctypes.c_int
         lib.gr_decode_attn_paged.argtypes = [DP, ctypes.POINTER(PagedCtx)] + [P] * 10
@@ -120,6 +136,10 @@ def load() -> ctypes.CDLL:
 
 
 # ---- the C entry points, same names and arguments -------------------------
+def gr_decode_attn_workspace_bytes(dims: Dims) -> int:
+    return load().gr_decode_attn_workspace_bytes(ctypes.byref(dims))
+
+
 def gr_decode_attn(dims: Dims, row_offset, q, ctx_k, ctx_v, ctx_len, beam_k, beam_v,
                    beam_path, beam_len, out, lse, stream) -> int:
     return load().gr_decode_attn(ctypes.byref(dims), row_offset, q, ctx_k, ctx_v, ctx_len,
@@ -194,12 +214,31 @@ def _stream_handle(stream) -> Optional[int]:
     return stream.cuda_stream or None
 
 
-def make_dims(q, ctx_k, beam_k, beam_path, W_max: int, scale: Optional[float] = None) -> Dims:
+def make_dims(q, ctx_k, beam_k, beam_path, W_max: int, scale: Optional[float] = None,
+              tiling=None) -> Dims:
     R, Hq, D = q.shape
     B, ctx_cap, Hkv, _ = ctx_k.shape
     return Dims(B=B, R=R, Hq=Hq, Hkv=Hkv, D=D, W_max=int(W_max), T_cap=beam_path.shape[1],
                 reserved=0, ctx_cap=ctx_cap, beam_cap=beam_k.shape[1],
-                scale=0.0 if scale is None else float(scale), flags=0)
+                scale=0.0 if scale is None else float(scale), flags=tiling_flags(tiling))
+
+
+def attach_workspace(dims: Dims, workspace, device):
+    """Point ``dims`` at a workspace of gr_decode_attn_workspace_bytes(dims)
+    bytes: ``workspace`` (a device tensor, zero-filled before its first use)
+    or, when None, a fresh zero-filled uint8 tensor.  Returns the tensor (or
+    None when the call needs no workspace); keep it alive until the call has
+    run."""
+    import torch
+    need = gr_decode_attn_workspace_bytes(dims)
+    if need == 0:
+        dims.workspace, dims.workspace_bytes = None, 0
+        return workspace
+    if workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=device)
+    dims.workspace = workspace.data_ptr()
+    dims.workspace_bytes = workspace.numel() * workspace.element_size()
+    return workspace
 
 
 def _check(q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path, beam_len, row_offset):
@@ -229,14 +268,17 @@ def _check(q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path, beam_len, row_of
 
 
 def _run(fn_name, q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path, beam_len, row_offset,
-         W_max, scale, out, lse, stream) -> Tuple:
+         W_max, scale, out, lse, stream, workspace=None, tiling=None) -> Tuple:
     import torch
     _check(q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path, beam_len, row_offset)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
-    dims = make_dims(q, ctx_k, beam_k, beam_path, W_max, scale)
+    dims = make_dims(q, ctx_k, beam_k, beam_path, W_max, scale,
+                     tiling if fn_name == "fused" else None)
+    if fn_name == "fused":
+        workspace = attach_workspace(dims, workspace, q.device)
     fn = gr_decode_attn if fn_name == "fused" else gr_decode_attn_generic
     st = fn(dims, _ptr(row_offset), _ptr(q), _ptr(ctx_k), _ptr(ctx_v), _ptr(ctx_len),
             _ptr(beam_k), _ptr(beam_v), _ptr(beam_path), _ptr(beam_len), _ptr(out), _ptr(lse),
@@ -248,15 +290,21 @@ def _run(fn_name, q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path, beam_len,
 
 
 def decode_attn(q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path, beam_len, row_offset,
-                W_max: int, scale: Optional[float] = None, out=None, lse=None, stream=None):
+                W_max: int, scale: Optional[float] = None, out=None, lse=None, stream=None,
+                workspace=None, tiling=None):
     """Fused shared-context / BeamPath / LSE-merge decode attention.
 
     Tensors as in include/gr_attn.h (bf16 / int32, contiguous, on the GPU).
-    ``W_max`` bounds every request's row count.  Returns (out bf16 [R,Hq,D],
-    lse fp32 [R,Hq]); enqueued on ``stream`` (default: torch's current one).
+    ``W_max`` bounds every request's row count.  ``workspace``: a device
+    tensor of at least gr_decode_attn_workspace_bytes bytes, zero-filled
+    before its first use and not shared by concurrent calls (None: a fresh
+    one per call).  ``tiling``: (nqt, nks[, n_split]) forces the work
+    decomposition (tuning and tests); None lets the library plan.  Returns
+    (out bf16 [R,Hq,D], lse fp32 [R,Hq]); enqueued on ``stream`` (default:
+    torch's current one).
     """
     return _run("fused", q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path, beam_len,
-                row_offset, W_max, scale, out, lse, stream)
+                row_offset, W_max, scale, out, lse, stream, workspace, tiling)
 
 
 def decode_attn_generic(q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path, beam_len,
@@ -269,7 +317,8 @@ def decode_attn_generic(q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path, bea
 
 def decode_attn_paged(q, k_pages, v_pages, page_table, page_size: int, ctx_len, beam_k, beam_v,
                       beam_path, beam_len, row_offset, W_max: int, ctx_cap: Optional[int] = None,
-                      scale: Optional[float] = None, out=None, lse=None, stream=None):
+                      scale: Optional[float] = None, out=None, lse=None, stream=None,
+                      workspace=None, tiling=None):
     """``decode_attn`` with the ContextKV in pages (include/gr_attn.h,
     gr_decode_attn_paged): k_pages / v_pages bf16 [n_pages][page_size][Hkv][D],
     page_table int32 [B][pages_per_req].  ``ctx_cap`` defaults to
@@ -301,7 +350,8 @@ def decode_attn_paged(q, k_pages, v_pages, page_table, page_size: int, ctx_len, 
     R, Hq, _ = q.shape
     dims = Dims(B=B, R=R, Hq=Hq, Hkv=Hkv, D=D, W_max=int(W_max), T_cap=beam_path.shape[1],
                 reserved=0, ctx_cap=cap, beam_cap=beam_k.shape[1],
-                scale=0.0 if scale is None else float(scale), flags=0)
+                scale=0.0 if scale is None else float(scale), flags=tiling_flags(tiling))
+    workspace = attach_workspace(dims, workspace, q.device)
     ctx = PagedCtx(k_pages=k_pages.data_ptr(), v_pages=v_pages.data_ptr(),
                    page_table=page_table.data_ptr(), page_size=int(page_size), pages_per_req=ppr,
                    n_pages=n_pages)

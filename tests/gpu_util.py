@@ -16,15 +16,17 @@ def log(msg: str):
     print(msg, flush=True)
 
 
-def run_lib(inp: I.Inputs, which: str = "fused", dev=None, scale=None):
-    """Run the library on ``inp``; return (out float32 numpy [R,Hq,D], lse numpy [R,Hq])."""
+def run_lib(inp: I.Inputs, which: str = "fused", dev=None, scale=None, tiling=None):
+    """Run the library on ``inp``; return (out float32 numpy [R,Hq,D], lse numpy [R,Hq]).
+    ``tiling`` = (nqt, nks[, n_split]) forces the fused kernel's work decomposition."""
     import torch
     from shared_prefix_beam_amd import gr_attn
     t = dev if dev is not None else I.to_torch(inp)
+    kw = dict(tiling=tiling) if which == "fused" else {}
     fn = gr_attn.decode_attn if which == "fused" else gr_attn.decode_attn_generic
     out, lse = fn(t["q"], t["ctx_k"], t["ctx_v"], t["ctx_len"], t["beam_k"], t["beam_v"],
                   t["beam_path"], t["beam_len"], t["row_offset"], W_max=int(max(inp.wl.W)),
-                  scale=scale)
+                  scale=scale, **kw)
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), lse.cpu().numpy()
 
@@ -49,24 +51,3 @@ def assert_parity(out, lse, ref_out, ref_lse, what=""):
     assert a <= MAX_ABS, f"{what}: max abs {a}"
     assert r <= MAX_REL, f"{what}: max rel {r}"
     assert l <= LSE_ABS, f"{what}: lse abs {l}"
-
-
-def sample_rows(inp: I.Inputs, n: int, seed: int = 0):
-    """Every request's first/last rows, rows at 64-row stack-tile edges, random rows."""
-    rng = np.random.default_rng(seed)
-    rows = set()
-    G = inp.wl.G
-    for b in range(inp.B):
-        r0, r1 = int(inp.row_offset[b]), int(inp.row_offset[b + 1])
-        if r1 == r0:
-            continue
-        rows.update((r0, r1 - 1))
-        for m in range(0, (r1 - r0) * G, 64):            # tile boundaries of the stacked rows
-            for w in (m // G - 1, m // G):
-                if 0 <= w < r1 - r0:
-                    rows.add(r0 + w)
-    rows = sorted(rows)
-    if len(rows) > n // 2:
-        rows = sorted(rng.choice(rows, size=n // 2, replace=False).tolist())
-    extra = rng.integers(0, inp.R, size=n - len(rows))
-    return sorted(set(rows) | set(int(x) for x in extra))

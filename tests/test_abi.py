@@ -31,15 +31,16 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_dims_struct_layout():
-    # int32 x8, int64 x2, float, int32 -> 56 bytes, int64 fields 8-aligned
-    assert ctypes.sizeof(gr_attn.Dims) == 56
+    # int32 x8, int64 x2, float, int32, pointer, uint64 -> 72 bytes, 8-aligned
+    assert ctypes.sizeof(gr_attn.Dims) == 72
     assert gr_attn.Dims.ctx_cap.offset == 32 and gr_attn.Dims.scale.offset == 48
+    assert gr_attn.Dims.workspace.offset == 56 and gr_attn.Dims.workspace_bytes.offset == 64
 
 
 def test_version_and_status_strings(lib):
     assert gr_attn.gr_version() >= 100
     assert gr_attn.gr_status_str(0) == "ok"
-    for code in (-1, -2, -3, -4, -5, -6):
+    for code in (-1, -2, -3, -4, -5, -6, -7):
         assert gr_attn.gr_status_str(code) != "unknown status"
 
 
@@ -71,6 +72,11 @@ def call(dims, **ptrs):
     (dict(scale=float("nan")), gr_attn.GR_ERR_DIMS),
     (dict(reserved=1), gr_attn.GR_ERR_DIMS),
     (dict(flags=2), gr_attn.GR_ERR_DIMS),
+    (dict(flags=gr_attn.tiling_flags((4, 1, 9))), gr_attn.GR_ERR_DIMS),
+    (dict(flags=gr_attn.tiling_flags((0, 1, 1))), gr_attn.GR_ERR_DIMS),
+    (dict(flags=gr_attn.tiling_flags((4, 1, 1)) | (1 << 24)), gr_attn.GR_ERR_DIMS),
+    (dict(flags=gr_attn.tiling_flags((3, 3, 1))), gr_attn.GR_ERR_UNSUPPORTED),
+    (dict(flags=gr_attn.tiling_flags((2, 4, 1))), gr_attn.GR_ERR_UNSUPPORTED),
     (dict(D=96), gr_attn.GR_ERR_UNSUPPORTED),
     (dict(Hq=32, Hkv=2), gr_attn.GR_ERR_UNSUPPORTED),
 ])
@@ -85,6 +91,46 @@ def test_null_and_alignment_rejected():
     assert call(good_dims(), ctx_k=P16 + 8) == gr_attn.GR_ERR_ALIGN
     assert call(good_dims(), out=P16 + 2) == gr_attn.GR_ERR_ALIGN
     assert call(good_dims(), lse=P16 + 2) == gr_attn.GR_ERR_ALIGN
+
+
+def split_dims(**over):
+    # 16 (request, KV head) pairs of 10 stacked rows and 1024 context tokens:
+    # far too few waves for the GPU, so each pair's context is split
+    d = dict(B=2, R=10, Hq=16, Hkv=8, D=128, W_max=5, T_cap=3, reserved=0, ctx_cap=1024,
+             beam_cap=16, scale=0.0, flags=0)
+    d.update(over)
+    return gr_attn.Dims(**d)
+
+
+def part_bytes(D):
+    return (D // 8 + 1) * 64 * 16       # one wave's partial: O^T fragments + stats
+
+
+def test_workspace_bytes():
+    f = gr_attn.gr_decode_attn_workspace_bytes
+    assert f(good_dims()) == 0                               # 2 context tiles: no split
+    assert f(split_dims()) > 0
+    assert f(good_dims(R=0, W_max=0)) == 0 and f(split_dims(Hq=12)) == 0
+    assert gr_attn.load().gr_decode_attn_workspace_bytes(None) == 0
+    # forced tilings: counters (256-byte aligned) + units x splits x waves partials
+    for nqt, nks, sp in ((4, 1, 1), (4, 1, 3), (2, 2, 8), (8, 1, 2)):
+        n = f(split_dims(flags=gr_attn.tiling_flags((nqt, nks, sp))))
+        units = 2 * 8 * -(-10 // (32 * nqt))
+        want = 0 if sp == 1 else ((units * 4 + 255) // 256) * 256 + units * sp * nqt * \
+            part_bytes(128)
+        assert n == want, (nqt, nks, sp, n, want)
+
+
+def test_workspace_rejected():
+    need = gr_attn.gr_decode_attn_workspace_bytes(split_dims())
+    assert call(split_dims()) == gr_attn.GR_ERR_WORKSPACE                     # NULL
+    assert call(split_dims(workspace=P16 * 16, workspace_bytes=need - 1)) == \
+        gr_attn.GR_ERR_WORKSPACE                                              # short
+    assert call(split_dims(workspace=P16 * 16 + 128, workspace_bytes=need)) == \
+        gr_attn.GR_ERR_WORKSPACE                                              # misaligned
+    # accepted: validation passes and only the (absent) device is refused
+    assert call(split_dims(workspace=P16 * 16, workspace_bytes=need)) in (
+        gr_attn.GR_ERR_DEVICE, gr_attn.GR_ERR_UNSUPPORTED)
 
 
 def test_empty_call_is_a_no_op():

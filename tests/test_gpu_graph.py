@@ -23,11 +23,17 @@ def test_decode_attn_graph_replays():
     lse = torch.empty(t["q"].shape[:2], dtype=torch.float32, device="cuda")
     q_other = torch.randn_like(t["q"].float()).to(torch.bfloat16)
     q_orig = t["q"].clone()
+    # these sizes split each pair's context over workgroups: one workspace,
+    # zeroed once, serves every call and replay (its counters reset themselves)
+    dims = gr_attn.make_dims(t["q"], t["ctx_k"], t["beam_k"], t["beam_path"], W_max)
+    need = gr_attn.gr_decode_attn_workspace_bytes(dims)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
 
     def call():
         gr_attn.decode_attn(t["q"], t["ctx_k"], t["ctx_v"], t["ctx_len"], t["beam_k"],
                             t["beam_v"], t["beam_path"], t["beam_len"], t["row_offset"],
-                            W_max=W_max, out=out, lse=lse)
+                            W_max=W_max, out=out, lse=lse, workspace=ws)
 
     # eager references for both query sets
     call()
@@ -60,6 +66,9 @@ def test_decode_attn_graph_replays():
         ref = ref_b if use_b else ref_a
         assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]), f"replay {i}"
         del junk
+    # every arrival counter is back at zero
+    n_counters = 3 * 8 * 2                       # pairs x query tiles of the (4,1) plan
+    assert int(ws[:4 * n_counters].view(torch.int32).abs().sum()) == 0
 
 
 def test_beam_step_graph_replays():

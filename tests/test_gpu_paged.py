@@ -6,14 +6,14 @@ import zlib
 import numpy as np
 import pytest
 
-from gpu_util import assert_parity, log, run_lib, sample_rows
+from gpu_util import assert_parity, log, run_lib
 from oracle import oracle as O
 from shared_prefix_beam_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
 
 
-def run_paged(inp, pg):
+def run_paged(inp, pg, tiling=None):
     import torch
     from shared_prefix_beam_amd import gr_attn
     t = I.to_torch(inp)
@@ -25,7 +25,7 @@ def run_paged(inp, pg):
         t["q"], bf(pg.k_pages), bf(pg.v_pages),
         torch.from_numpy(pg.page_table.astype(np.int32)).cuda(), pg.page_size, t["ctx_len"],
         t["beam_k"], t["beam_v"], t["beam_path"], t["beam_len"], t["row_offset"],
-        W_max=int(max(inp.wl.W)), ctx_cap=inp.ctx_cap)
+        W_max=int(max(inp.wl.W)), ctx_cap=inp.ctx_cap, tiling=tiling)
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), lse.cpu().numpy()
 
@@ -51,11 +51,17 @@ def test_paged_ragged_all_rows(page_size):
         "paged and dense results differ"
 
 
-def test_paged_d64():
-    inp = ragged(D=64, Hq=8, Hkv=4, seed=64)
+@pytest.mark.parametrize("Hq,Hkv", [(8, 4), (16, 4), (16, 2)], ids=["g2", "g4", "g8"])
+def test_paged_d64(Hq, Hkv):
+    inp = ragged(D=64, Hq=Hq, Hkv=Hkv, seed=64 + Hq + Hkv)
     pg = I.to_paged(inp, 16, seed=65)
-    log(f"[paged] D=64 page 16 R={inp.R}")
+    log(f"[paged] D=64 G={Hq // Hkv} page 16 R={inp.R}")
     out, lse = run_paged(inp, pg)
+    ref_out, ref_lse = O.decode_attn_paged(inp.q, pg.k_pages, pg.v_pages, pg.page_table, 16,
+                                           inp.ctx_len, inp.beam_k, inp.beam_v, inp.beam_path,
+                                           inp.beam_len, inp.row_offset, ctx_cap=inp.ctx_cap,
+                                           scale=inp.scale)
+    assert_parity(out, lse, ref_out, ref_lse, f"paged d64 g{Hq // Hkv}")
     dense_out, dense_lse = run_lib(inp, "fused")
     assert np.array_equal(out, dense_out) and np.array_equal(lse, dense_lse)
 
@@ -63,15 +69,15 @@ def test_paged_d64():
 TILINGS = [(128, 8, 1), (128, 4, 1), (128, 4, 2), (128, 2, 2), (64, 4, 1), (64, 2, 2), (64, 2, 4)]
 
 
+@pytest.mark.parametrize("split", [1, 3], ids=["s1", "s3"])
 @pytest.mark.parametrize("tiling", TILINGS, ids=[f"d{d}_q{a}_k{c}" for d, a, c in TILINGS])
-def test_paged_every_tiling(tiling, monkeypatch):
+def test_paged_every_tiling(tiling, split):
     D, nqt, nks = tiling
-    monkeypatch.setenv("GR_ATTN_TILE", f"{nqt},{nks}")
     inp = ragged(D=D, Hq=16 if D == 128 else 8, Hkv=8 if D == 128 else 4, seed=nqt * 7 + nks)
     pg = I.to_paged(inp, 16, seed=3)
-    log(f"[paged] tiling {tiling}")
-    out, lse = run_paged(inp, pg)
-    dense_out, dense_lse = run_lib(inp, "fused")
+    log(f"[paged] tiling {tiling} split {split}")
+    out, lse = run_paged(inp, pg, tiling=(nqt, nks, split))
+    dense_out, dense_lse = run_lib(inp, "fused", tiling=(nqt, nks, split))
     assert np.array_equal(out, dense_out) and np.array_equal(lse, dense_lse)
 
 
@@ -81,10 +87,9 @@ def test_paged_workloads(cfg, page_size):
     pg = I.to_paged(inp, page_size, seed=cfg)
     log(f"[paged] workload {cfg} page {page_size} R={inp.R}")
     out, lse = run_paged(inp, pg)
-    rows = sample_rows(inp, 64, seed=cfg)
     ref_out, ref_lse = O.decode_attn_paged(inp.q, pg.k_pages, pg.v_pages, pg.page_table,
                                            page_size, inp.ctx_len, inp.beam_k, inp.beam_v,
                                            inp.beam_path, inp.beam_len, inp.row_offset,
-                                           ctx_cap=inp.ctx_cap, scale=inp.scale, rows=rows)
+                                           ctx_cap=inp.ctx_cap, scale=inp.scale)
     assert np.isfinite(out).all()
-    assert_parity(out[rows], lse[rows], ref_out, ref_lse, f"paged cfg{cfg}")
+    assert_parity(out, lse, ref_out, ref_lse, f"paged cfg{cfg}")

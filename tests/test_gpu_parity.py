@@ -8,13 +8,14 @@ import zlib
 import numpy as np
 import pytest
 
-from gpu_util import assert_parity, log, run_lib, sample_rows
+from gpu_util import assert_parity, log, run_lib
 from oracle import oracle as O
 from shared_prefix_beam_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
 
 _cache = {}
+_ref = {}
 
 
 def workload(cfg):
@@ -23,18 +24,24 @@ def workload(cfg):
     return _cache[cfg]
 
 
+def workload_ref(cfg):
+    """The oracle's result on every row of the workload (computed once)."""
+    if cfg not in _ref:
+        _ref[cfg] = O.decode_attn_inputs(workload(cfg))
+    return _ref[cfg]
+
+
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("which", ["fused", "generic"])
 def test_workload_parity(cfg, which):
-    """Full-size workloads; the oracle evaluates a sample of rows (all rows
-    for the tiny workload) including every tile edge."""
+    """Full-size workloads, in the launch configuration the benchmark times:
+    every output row and head against the fp64 oracle."""
     inp = workload(cfg)
     log(f"[parity] workload {cfg} ({inp.wl.name}) path={which} R={inp.R}")
     out, lse = run_lib(inp, which)
-    rows = list(range(inp.R)) if cfg == 1 else sample_rows(inp, 192, seed=cfg)
-    ref_out, ref_lse = O.decode_attn_inputs(inp, rows=rows)
+    ref_out, ref_lse = workload_ref(cfg)
     assert np.isfinite(out).all(), "NaN/inf anywhere in the output"
-    assert_parity(out[rows], lse[rows], ref_out, ref_lse, f"cfg{cfg}/{which}")
+    assert_parity(out, lse, ref_out, ref_lse, f"cfg{cfg}/{which}")
 
 
 SMALL = [
@@ -52,6 +59,18 @@ SMALL = [
     ("no_keys_at_all", 1, 16, 8, 128, [3], [0], [0], dict(ctx_cap=32, T_cap=2)),
     ("dup_paths", 2, 16, 8, 128, [60, 40], [256, 130], [3, 3], dict(dup_frac=0.3)),
     ("sharp_q8", 2, 16, 8, 128, [30, 20], [900, 400], [3, 4], dict(q_std=8.0)),
+    # group sizes that do not divide a wave's 32 query columns: per-lane gathers
+    ("g3", 2, 24, 8, 128, [30, 11], [700, 65], [3, 2], {}),
+    ("g5", 2, 40, 8, 128, [13, 7], [300, 90], [4, 1], {}),
+    ("g6", 2, 48, 8, 128, [22, 9], [500, 120], [3, 5], {}),
+    ("g7", 1, 56, 8, 128, [10], [260], [3], {}),
+    # D = 64 at the larger groups (G = 8: fewer beams per wave than rows per load)
+    ("d64_g4", 2, 16, 4, 64, [21, 40], [300, 97], [3, 2], {}),
+    ("d64_g8", 2, 16, 2, 64, [17, 40], [333, 64], [3, 4], {}),
+    ("d64_g8_mha_heads", 1, 64, 8, 64, [12], [150], [5], {}),
+    # BeamPath tables larger than the staged 4 KB (entries loaded per lane)
+    ("ptab_overflow_g1", 1, 8, 8, 128, [150], [300], [9], {}),
+    ("ptab_overflow_g2", 2, 16, 8, 128, [100, 64], [200, 129], [17, 12], {}),
 ]
 
 
@@ -68,22 +87,37 @@ def test_small_shapes_all_rows(case, which):
 
 
 TILINGS = [(128, 8, 1), (128, 4, 1), (128, 4, 2), (128, 2, 2), (64, 4, 1), (64, 2, 2), (64, 2, 4)]
+SPLITS = [1, 2, 3, 8]
 
 
+@pytest.mark.parametrize("split", SPLITS, ids=[f"s{s}" for s in SPLITS])
 @pytest.mark.parametrize("tiling", TILINGS, ids=[f"d{d}_q{a}_k{c}" for d, a, c in TILINGS])
-def test_every_tiling_ragged(tiling, monkeypatch):
-    """Each compiled (query tile, key streams) shape, forced through the
-    planner override, on ragged requests: partial context tiles, partial
-    query tiles, streams with unequal tile counts and an empty stream."""
+def test_every_tiling_ragged(tiling, split):
+    """Each compiled (query tile, key streams) shape with the context split
+    over 1, 2, 3 and 8 workgroups, forced per call, on ragged requests:
+    partial context tiles, partial query tiles, streams and splits with
+    unequal tile counts, empty ones (the 33-token context has 2 tiles) and
+    beam steps spread over the streams of several workgroups."""
     D, nqt, nks = tiling
-    monkeypatch.setenv("GR_ATTN_TILE", f"{nqt},{nks}")
     Hq, Hkv = (16, 8) if D == 128 else (8, 4)
     inp = I.custom(B=3, Hq=Hq, Hkv=Hkv, D=D, W=[37, 5, 130], ctx_len=[1000, 33, 517],
-                   beam_len=[3, 1, 5], seed=100 + nqt * 10 + nks)
-    log(f"[parity] tiling D={D} NQT={nqt} NKS={nks} R={inp.R}")
-    out, lse = run_lib(inp, "fused")
+                   beam_len=[3, 1, 5], seed=100 + nqt * 10 + nks + 1000 * split)
+    log(f"[parity] tiling D={D} NQT={nqt} NKS={nks} split={split} R={inp.R}")
+    out, lse = run_lib(inp, "fused", tiling=(nqt, nks, split))
     ref_out, ref_lse = O.decode_attn_inputs(inp)
-    assert_parity(out, lse, ref_out, ref_lse, f"tiling {tiling}")
+    assert_parity(out, lse, ref_out, ref_lse, f"tiling {tiling} split {split}")
+
+
+def test_split_is_deterministic():
+    """The last workgroup of a split unit combines the partials in ascending
+    split order whichever workgroup it is: repeated calls are bitwise equal."""
+    inp = I.custom(B=2, Hq=16, Hkv=8, D=128, W=[64, 33], ctx_len=[2000, 700],
+                   beam_len=[3, 2], seed=77)
+    log("[parity] split determinism")
+    a = run_lib(inp, "fused", tiling=(4, 1, 8))
+    for _ in range(3):
+        b = run_lib(inp, "fused", tiling=(4, 1, 8))
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
 def test_rising_scores_take_exact_sweep():
