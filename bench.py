@@ -187,7 +187,8 @@ def write_profile_summaries(d: str):
     f_fetch, copy_fetch_kib = _copy_factor(os.path.join(d, "copy_fetch"), "FETCH_SIZE")
     f_write, copy_write_kib = _copy_factor(os.path.join(d, "copy_write"), "WRITE_SIZE")
     sha = kernel_hash()
-    for which, cfg in (("primary", PRIMARY), ("secondary", SECONDARY)):
+    for which, cfg in (("primary", PRIMARY), ("secondary", SECONDARY), ("cfg1", 1), ("cfg3", 3),
+                       ("cfg5", 5)):
         if not os.path.isdir(os.path.join(d, f"trace_{which}")):
             continue                                # not profiled in this folder
         wl = I.WORKLOADS[cfg]
@@ -453,7 +454,7 @@ def measure(cfg: int, steps: int, warmup: int, page_size=None, reps: int = 5,
         launch.append(ev0.elapsed_time(ev1) / steps)
 
     # cold per-call latency: a 512 MB write between calls evicts L2 and MALL
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = torch.empty(512 << 20 if latency_calls else 1, dtype=torch.uint8, device="cuda")
     lat = []
     for i in range(latency_calls):
         flush.fill_(i & 255)
@@ -482,7 +483,7 @@ def measure(cfg: int, steps: int, warmup: int, page_size=None, reps: int = 5,
     srt = sorted(launch)
     return dict(inp=inp, nbytes=nbytes, flops=flops, ms_per_step=ms_per_step,
                 launch_ms=launch[0], launch_median_ms=srt[len(srt) // 2], launch_min_ms=srt[0],
-                launch_reps_ms=launch, latency_ms=sorted(lat)[len(lat) // 2],
+                launch_reps_ms=launch, latency_ms=sorted(lat)[len(lat) // 2] if lat else None,
                 n_sets=n_sets, spot_abs=spot, spot_lse=spot_lse, spot_rows=len(rows),
                 workspace_bytes=ws_bytes)
 
@@ -502,12 +503,12 @@ def config_entry(cfg: int, r) -> dict:
             "launch_us": r["launch_ms"] * 1e3, "launch_us_median": r["launch_median_ms"] * 1e3,
             "launch_us_min": r["launch_min_ms"] * 1e3,
             "launch_us_reps": [round(x * 1e3, 3) for x in r["launch_reps_ms"]],
-            "latency_us_cold": r["latency_ms"] * 1e3,
+            "latency_us_cold": r["latency_ms"] * 1e3 if r["latency_ms"] is not None else None,
             "beam_rows_per_s": inp.R / t, "hbm_GBps": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
             "TFLOPs": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS,
             "bound": "hbm" if ai < RIDGE else "mfma", "flop_per_byte": ai,
             "algorithmic_bytes": r["nbytes"], "algorithmic_flops": r["flops"],
-            "workspace_bytes": r["workspace_bytes"],
+            "workspace_bytes": r["workspace_bytes"], "traffic": recorded_traffic(inp.wl.name),
             "spot_check": {"rows": r["spot_rows"], "max_abs": r["spot_abs"],
                            "lse_abs": r["spot_lse"]}}
 

@@ -107,11 +107,12 @@ typedef struct gr_decode_attn_dims {
  * bytes (0 when the call is planned without a cross-workgroup context split).
  * The pages split the long ContextKV over several workers (Split-KV:
  * GR-Inference blog, section on kernel design); when the (request, KV head)
- * pairs alone cannot fill the GPU, the library splits each pair's context
- * over several workgroups, which leave fp32 partial results (unnormalised
- * output, running maximum and sums) in the workspace, and the last of them to
- * finish combines them by log-sum-exp.  Layout: arrival counters first, then
- * the partials; it is private to the library.
+ * pairs alone cannot fill the GPU and each pair has few query rows for its
+ * context length, the library splits each pair's context over several
+ * workgroups, which leave fp32 partial results (unnormalised output, running
+ * maximum and sums) in the workspace, and the last of them to finish combines
+ * them by log-sum-exp.  Layout: arrival counters first, then the partials;
+ * it is private to the library.
  *
  * Contract: the caller allocates at least this many bytes, 256-byte aligned,
  * and ZERO-FILLS it once before its first use (the counters must start at

@@ -1002,29 +1002,38 @@ void fused_decode_attn(const Params p)
     // Every workgroup of the unit leaves its waves' (O, max, sums) in the
     // workspace in lane order, then counts itself in; the last to arrive
     // resets the counter for the next call and combines all n_split partials
-    // in ascending split order (its own from registers), so the result does
-    // not depend on which workgroup finishes last.  The device-scope fences
-    // make the partials visible to that workgroup before its count returns.
+    // in ascending split order, its own included and read back like the
+    // others, so the result does not depend on which workgroup finishes
+    // last.  Partials are written and read with device-scope (sc1) accesses,
+    // which are coherent across XCDs without an L2 writeback: the writer
+    // waits for its stores to complete before it counts itself in, and the
+    // last workgroup reads only after its count has returned.
     if (p.n_split > 1) {
         __shared__ int s_last;
         const int unit = pair * p.n_qt + qtile;
         constexpr int PB = fused_part_bytes(D);
         constexpr int NV = D / 8;                  // f32x4 per lane of a wave's O^T
-        char *const part_u = p.ws_part + (size_t)unit * p.n_split * NQT * PB;
+        constexpr int SC1 = 16;                    // cache policy: device scope
+        const int unit_bytes = p.n_split * NQT * PB;
+        const __amdgpu_buffer_rsrc_t part = __builtin_amdgcn_make_buffer_rsrc(
+            p.ws_part + (size_t)unit * unit_bytes, 0, unit_bytes, 0x00020000);
         if (ks == 0 && wave_live) {
-            char *mine = part_u + ((size_t)split * NQT + qt) * PB + 16 * lane;
+            const int mine = (split * NQT + qt) * PB + 16 * lane;
             if (m_ref != NEG_INF) {                // nothing to add otherwise
 #pragma unroll
                 for (int db = 0; db < Gm::DB; ++db)
 #pragma unroll
                     for (int rg = 0; rg < 4; ++rg)
-                        *reinterpret_cast<f32x4 *>(mine + (db * 4 + rg) * 1024) =
-                            f32x4{o[db][4 * rg], o[db][4 * rg + 1], o[db][4 * rg + 2],
-                                  o[db][4 * rg + 3]};
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            __builtin_bit_cast(u32x4, f32x4{o[db][4 * rg], o[db][4 * rg + 1],
+                                                            o[db][4 * rg + 2], o[db][4 * rg + 3]}),
+                            part, mine + (db * 4 + rg) * 1024, 0, SC1);
             }
-            *reinterpret_cast<f32x4 *>(mine + NV * 1024) = f32x4{m_ref, l_run, l_lse, 0.f};
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u32x4, f32x4{m_ref, l_run, l_lse, 0.f}), part,
+                mine + NV * 1024, 0, SC1);
         }
-        __threadfence();
+        wait_vm<0>();                              // this wave's partial is complete
         __syncthreads();
         if (tid == 0) {
             const int last = atomicAdd(p.ws_count + unit, 1) == p.n_split - 1;
@@ -1035,53 +1044,37 @@ void fused_decode_attn(const Params p)
         __syncthreads();
         if (!s_last)
             return;
-        __threadfence();
         if (ks == 0 && wave_live) {
-            const float m_own = m_ref, lr_own = l_run, ll_own = l_lse;
             float mm = NEG_INF, lr = 0.f, ll = 0.f;
 #pragma unroll
             for (int db = 0; db < Gm::DB; ++db)
-                acc[db] = f32x16{};                // the combined O^T
+                o[db] = f32x16{};                  // the combined O^T
 #pragma unroll 1
             for (int sp = 0; sp < p.n_split; ++sp) {
-                const char *src = part_u + ((size_t)sp * NQT + qt) * PB + 16 * lane;
-                float ms = m_own, lrs = lr_own, lls = ll_own;
-                if (sp != split) {
-                    const f32x4 st = *reinterpret_cast<const f32x4 *>(src + NV * 1024);
-                    ms = st[0];
-                    lrs = st[1];
-                    lls = st[2];
-                }
+                const int src = (sp * NQT + qt) * PB + 16 * lane;
+                const f32x4 st = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(part, src + NV * 1024, 0, SC1));
+                const float ms = st[0];
                 if (ms == NEG_INF)
                     continue;                      // an empty partial
                 const float mn = __builtin_fmaxf(mm, ms);
                 const float a = mm == NEG_INF ? 0.f : exp2_fast(mm - mn);
                 const float bw = exp2_fast(ms - mn);
-                if (sp == split) {
 #pragma unroll
-                    for (int db = 0; db < Gm::DB; ++db)
+                for (int db = 0; db < Gm::DB; ++db)
 #pragma unroll
-                        for (int e = 0; e < 16; ++e)
-                            acc[db][e] = acc[db][e] * a + o[db][e] * bw;
-                } else {
+                    for (int rg = 0; rg < 4; ++rg) {
+                        const f32x4 v = __builtin_bit_cast(
+                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                       part, src + (db * 4 + rg) * 1024, 0, SC1));
 #pragma unroll
-                    for (int db = 0; db < Gm::DB; ++db)
-#pragma unroll
-                        for (int rg = 0; rg < 4; ++rg) {
-                            const f32x4 v =
-                                *reinterpret_cast<const f32x4 *>(src + (db * 4 + rg) * 1024);
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                acc[db][4 * rg + e] = acc[db][4 * rg + e] * a + v[e] * bw;
-                        }
-                }
+                        for (int e = 0; e < 4; ++e)
+                            o[db][4 * rg + e] = o[db][4 * rg + e] * a + v[e] * bw;
+                    }
                 mm = mn;
-                lr = lr * a + lrs * bw;
-                ll = ll * a + lls * bw;
+                lr = lr * a + st[1] * bw;
+                ll = ll * a + st[2] * bw;
             }
-#pragma unroll
-            for (int db = 0; db < Gm::DB; ++db)
-                o[db] = acc[db];
             m_ref = mm;
             l_run = lr;
             l_lse = ll;

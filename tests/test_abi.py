@@ -94,9 +94,10 @@ def test_null_and_alignment_rejected():
 
 
 def split_dims(**over):
-    # 16 (request, KV head) pairs of 10 stacked rows and 1024 context tokens:
-    # far too few waves for the GPU, so each pair's context is split
-    d = dict(B=2, R=10, Hq=16, Hkv=8, D=128, W_max=5, T_cap=3, reserved=0, ctx_cap=1024,
+    # 16 (request, KV head) pairs of 10 stacked rows and 8192 context tokens:
+    # far too few waves for the GPU, and partials much smaller than the
+    # context, so each pair's context is split
+    d = dict(B=2, R=10, Hq=16, Hkv=8, D=128, W_max=5, T_cap=3, reserved=0, ctx_cap=8192,
              beam_cap=16, scale=0.0, flags=0)
     d.update(over)
     return gr_attn.Dims(**d)
@@ -372,3 +373,4 @@ def test_trie_null_descriptor_rejected():
 
 def test_trie_empty_batch_is_a_no_op():
     assert trie_call(select_dims(B=0, R_old=0, R_new=0), trie_desc()) == gr_attn.GR_OK
+

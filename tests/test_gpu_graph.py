@@ -23,9 +23,11 @@ def test_decode_attn_graph_replays():
     lse = torch.empty(t["q"].shape[:2], dtype=torch.float32, device="cuda")
     q_other = torch.randn_like(t["q"].float()).to(torch.bfloat16)
     q_orig = t["q"].clone()
-    # these sizes split each pair's context over workgroups: one workspace,
-    # zeroed once, serves every call and replay (its counters reset themselves)
-    dims = gr_attn.make_dims(t["q"], t["ctx_k"], t["beam_k"], t["beam_path"], W_max)
+    # each pair's context split over 4 workgroups: one workspace, zeroed
+    # once, serves every call and replay (its counters reset themselves)
+    tiling = (4, 1, 4)
+    dims = gr_attn.make_dims(t["q"], t["ctx_k"], t["beam_k"], t["beam_path"], W_max,
+                             tiling=tiling)
     need = gr_attn.gr_decode_attn_workspace_bytes(dims)
     assert need > 0
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
@@ -33,7 +35,7 @@ def test_decode_attn_graph_replays():
     def call():
         gr_attn.decode_attn(t["q"], t["ctx_k"], t["ctx_v"], t["ctx_len"], t["beam_k"],
                             t["beam_v"], t["beam_path"], t["beam_len"], t["row_offset"],
-                            W_max=W_max, out=out, lse=lse, workspace=ws)
+                            W_max=W_max, out=out, lse=lse, workspace=ws, tiling=tiling)
 
     # eager references for both query sets
     call()

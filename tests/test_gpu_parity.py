@@ -68,6 +68,10 @@ SMALL = [
     ("d64_g4", 2, 16, 4, 64, [21, 40], [300, 97], [3, 2], {}),
     ("d64_g8", 2, 16, 2, 64, [17, 40], [333, 64], [3, 4], {}),
     ("d64_g8_mha_heads", 1, 64, 8, 64, [12], [150], [5], {}),
+    # few beams against long contexts: the planner splits each pair's context
+    # over several workgroups (partials combined through the workspace)
+    ("long_ctx_few_beams", 1, 16, 8, 128, [4], [8000], [3], {}),
+    ("long_ctx_g4", 2, 32, 8, 128, [3, 5], [6000, 3000], [5, 2], {}),
     # BeamPath tables larger than the staged 4 KB (entries loaded per lane)
     ("ptab_overflow_g1", 1, 8, 8, 128, [150], [300], [9], {}),
     ("ptab_overflow_g2", 2, 16, 8, 128, [100, 64], [200, 129], [17, 12], {}),
