@@ -141,6 +141,29 @@ int gr_decode_attn(const gr_decode_attn_dims *dims, const int32_t *row_offset,
                    float *lse, void *stream);
 
 /*
+ * gr_decode_attn for callers that cannot allocate device memory: code under
+ * HIP graph capture, serving loops and harnesses that forbid allocation.
+ * Same arguments, results, ownership of the caller's buffers and errors as
+ * gr_decode_attn, except that dims->workspace and dims->workspace_bytes are
+ * ignored: when the call is planned with a context split, its counters and
+ * partials live in a scratch array inside the library, one per device (16 MiB,
+ * held until the process ends; its address is looked up once per device on
+ * that device's first call, which also clears its counters with a kernel on
+ * `stream`).  A call whose split would not fit the scratch (more than 16384
+ * (request, KV head, query tile) units, or partials beyond 16 MiB - 64 KiB)
+ * returns GR_ERR_WORKSPACE and enqueues nothing.  Nothing is allocated or
+ * freed.  Every call on one device shares that device's scratch: two calls
+ * that can run at the same time on one device (different streams, or
+ * different host threads) race and may give wrong results; callers order
+ * them (one stream) or use gr_decode_attn with a workspace each.
+ */
+int gr_decode_attn_noalloc(const gr_decode_attn_dims *dims, const int32_t *row_offset,
+                           const void *q, const void *ctx_k, const void *ctx_v,
+                           const int32_t *ctx_len, const void *beam_k, const void *beam_v,
+                           const int32_t *beam_path, const int32_t *beam_len, void *out,
+                           float *lse, void *stream);
+
+/*
  * The same operation computed the way a generic decode-attention kernel
  * does it: every (row, head) independently reads its request's whole
  * ContextKV (SID-GR README, section "Performance Breakdown": the

@@ -314,6 +314,51 @@ int gr_decode_attn(const gr_decode_attn_dims *d, const int32_t *row_offset, cons
     return e == hipSuccess ? GR_OK : GR_ERR_LAUNCH;
 }
 
+int gr_decode_attn_noalloc(const gr_decode_attn_dims *d, const int32_t *row_offset,
+                           const void *q, const void *ctx_k, const void *ctx_v,
+                           const int32_t *ctx_len, const void *beam_k, const void *beam_v,
+                           const int32_t *beam_path, const int32_t *beam_len, void *out,
+                           float *lse, void *stream)
+{
+    int st = validate(d);
+    if (st != GR_OK)
+        return st;
+    st = validate_buffers(d, row_offset, q, ctx_k, ctx_v, ctx_len, beam_k, beam_v, beam_path,
+                          beam_len, out, lse);
+    if (st != GR_OK)
+        return st;
+    if (d->R == 0 || d->B == 0 || d->W_max == 0)
+        return GR_OK;
+    gr::Params p = make_params(d, row_offset, q, ctx_k, ctx_v, ctx_len, beam_k, beam_v,
+                               beam_path, beam_len, out, lse);
+    const Plan pl = plan(d);
+    if (pl.grid < 0)
+        return pl.grid == -2 ? GR_ERR_UNSUPPORTED : GR_ERR_DIMS;
+    p.n_qt = pl.n_qt;
+    p.n_split = pl.n_split;
+    if (pl.grid == 0)
+        return GR_OK;
+    // the split's counters and partials must fit the fixed scratch layout
+    const size_t units = static_cast<size_t>(d->B) * d->Hkv * pl.n_qt;
+    const size_t part = units * pl.n_split * pl.nqt * static_cast<size_t>(gr::fused_part_bytes(d->D));
+    if (pl.n_split > 1 && (units * sizeof(int32_t) > gr::NOALLOC_COUNTER_BYTES ||
+                           part > gr::NOALLOC_SCRATCH_BYTES - gr::NOALLOC_COUNTER_BYTES))
+        return GR_ERR_WORKSPACE;
+    st = device_ok();
+    if (st != GR_OK)
+        return st;
+    if (pl.n_split > 1) {
+        void *sp = nullptr;
+        if (gr::noalloc_scratch(&sp, static_cast<hipStream_t>(stream)) != hipSuccess)
+            return GR_ERR_DEVICE;
+        p.ws_count = static_cast<int32_t *>(sp);
+        p.ws_part = static_cast<char *>(sp) + gr::NOALLOC_COUNTER_BYTES;
+    }
+    const hipError_t e =
+        gr::launch_fused(p, pl.nqt, pl.nks, pl.grid, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GR_OK : GR_ERR_LAUNCH;
+}
+
 int gr_decode_attn_paged(const gr_decode_attn_dims *d, const gr_paged_ctx *c,
                          const int32_t *row_offset, const void *q, const int32_t *ctx_len,
                          const void *beam_k, const void *beam_v, const int32_t *beam_path,

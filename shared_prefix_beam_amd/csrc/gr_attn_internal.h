@@ -124,6 +124,14 @@ inline int fused_lds_bytes(int D, int nqt, int nks)
 // wave's own lane order (16-byte vectors, lane-contiguous).
 constexpr int fused_part_bytes(int D) { return (D / 8 + 1) * 64 * 16; }
 hipError_t launch_fused(const Params &p, int nqt, int nks, int grid, hipStream_t s);
+// Scratch of gr_decode_attn_noalloc, per device: fixed layout, the split
+// counters in the first NOALLOC_COUNTER_BYTES (never reused for partials, so
+// they stay zero between calls), the partials after them.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)16 << 20;
+constexpr size_t NOALLOC_COUNTER_BYTES = (size_t)64 << 10;
+// The current device's scratch address (looked up once per device; the
+// counters are cleared by a kernel on `s` before the first use).
+hipError_t noalloc_scratch(void **out, hipStream_t s);
 hipError_t launch_generic(const Params &p, hipStream_t s);
 hipError_t launch_check(const MetaCheck &c, hipStream_t s);
 hipError_t launch_beam_step(const StepParams &p, hipStream_t s);

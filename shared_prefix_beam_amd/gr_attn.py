@@ -37,8 +37,8 @@ def tiling_flags(tiling) -> int:
     split = rest[0] if rest else 1
     return GR_FLAG_TILING | int(nqt) | (int(nks) << 8) | (int(split) << 16)
 
-EXPORTS = ("gr_decode_attn_workspace_bytes", "gr_decode_attn", "gr_decode_attn_generic",
-           "gr_decode_attn_paged",
+EXPORTS = ("gr_decode_attn_workspace_bytes", "gr_decode_attn", "gr_decode_attn_noalloc",
+           "gr_decode_attn_generic", "gr_decode_attn_paged",
            "gr_check_metadata", "gr_beam_step", "gr_beam_select_workspace_bytes",
            "gr_beam_select", "gr_beam_select_trie", "gr_status_str", "gr_version")
 
@@ -107,7 +107,7 @@ def load() -> ctypes.CDLL:
         P = ctypes.c_void_p
         DP = ctypes.POINTER(Dims)
         attn_args = [DP, P, P, P, P, P, P, P, P, P, P, P, P]
-        for name in ("gr_decode_attn", "gr_decode_attn_generic"):
+        for name in ("gr_decode_attn", "gr_decode_attn_noalloc", "gr_decode_attn_generic"):
             fn = getattr(lib, name)
             fn.argtypes = attn_args
             fn.restype = ctypes.c_int
@@ -144,6 +144,13 @@ def gr_decode_attn(dims: Dims, row_offset, q, ctx_k, ctx_v, ctx_len, beam_k, bea
                    beam_path, beam_len, out, lse, stream) -> int:
     return load().gr_decode_attn(ctypes.byref(dims), row_offset, q, ctx_k, ctx_v, ctx_len,
                                  beam_k, beam_v, beam_path, beam_len, out, lse, stream)
+
+
+def gr_decode_attn_noalloc(dims: Dims, row_offset, q, ctx_k, ctx_v, ctx_len, beam_k, beam_v,
+                           beam_path, beam_len, out, lse, stream) -> int:
+    return load().gr_decode_attn_noalloc(ctypes.byref(dims), row_offset, q, ctx_k, ctx_v,
+                                         ctx_len, beam_k, beam_v, beam_path, beam_len, out,
+                                         lse, stream)
 
 
 def gr_decode_attn_generic(dims: Dims, row_offset, q, ctx_k, ctx_v, ctx_len, beam_k, beam_v,

@@ -100,4 +100,16 @@ hipError_t launch_beam_select(const SelParams &p, hipStream_t)
     return hipSuccess;
 }
 
+// The no-alloc scratch: a host array standing in for the device one, of the
+// same size, so that the stubbed launch can check the split's layout in it.
+static char g_scratch[NOALLOC_SCRATCH_BYTES] __attribute__((aligned(256)));
+
+hipError_t noalloc_scratch(void **out, hipStream_t)
+{
+    *out = g_scratch;
+    g_call.workspace = g_scratch;
+    g_call.workspace_bytes = NOALLOC_SCRATCH_BYTES;
+    return hipSuccess;
+}
+
 }  // namespace gr

@@ -85,6 +85,14 @@ static int fuzz_decode_attn(int iters)
             ++ok;
         if (st == GR_OK && need > 0)
             CHECK(d.workspace && d.workspace_bytes >= need);
+        // the no-alloc variant: the split goes to the library's scratch
+        {
+            const StubCall saved = g_call;
+            st = gr_decode_attn_noalloc(&d, I, P, P, P, I, P, P, I, I, fake(3), (float *)fake(4),
+                                        nullptr);
+            CHECK(known_status(st));
+            g_call = saved;
+        }
         // paged: the same dims through a page table
         gr_paged_ctx c{P, P, I, pick({0, 8, 16, 32, 48}), pick({0, 1, 64, 300}),
                        pick64({0, 1, 1000, 1LL << 32})};

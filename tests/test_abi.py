@@ -374,3 +374,15 @@ def test_trie_null_descriptor_rejected():
 def test_trie_empty_batch_is_a_no_op():
     assert trie_call(select_dims(B=0, R_old=0, R_new=0), trie_desc()) == gr_attn.GR_OK
 
+
+def test_noalloc_rejects_split_beyond_scratch():
+    # 64 requests x 8 KV heads x 15 query tiles forced into 8 splits: partials
+    # of ~1 GB cannot fit the 16 MiB scratch; refused before any device access
+    d = good_dims(B=64, R=64 * 900, W_max=900, ctx_cap=2048, flags=gr_attn.tiling_flags((4, 1, 8)))
+    st = gr_attn.gr_decode_attn_noalloc(d, *([P16] * 11), None)
+    assert st == gr_attn.GR_ERR_WORKSPACE
+    # without a split there is nothing to place: validation passes, the
+    # missing device is what is refused
+    d = good_dims(flags=gr_attn.tiling_flags((4, 1, 1)))
+    assert gr_attn.gr_decode_attn_noalloc(d, *([P16] * 11), None) in (
+        gr_attn.GR_ERR_DEVICE, gr_attn.GR_ERR_UNSUPPORTED)
