@@ -379,7 +379,9 @@ def measure(cfg: int, steps: int, warmup: int, page_size=None, reps: int = 5,
         base["page_table"] = torch.from_numpy(pg.page_table.astype(np.int32)).cuda()
     footprint = sum(t.numel() * t.element_size() for t in base.values()) \
         + base["q"].numel() * 2 + base["q"].shape[0] * base["q"].shape[1] * 4
-    n_sets = max(2, int(np.ceil(2 * MALL_BYTES / footprint)) + 1)
+    # enough copies that each step reads HBM, at most 64 (a workload this
+    # small is bound by launch latency, not by where its bytes come from)
+    n_sets = min(64, max(2, int(np.ceil(2 * MALL_BYTES / footprint)) + 1))
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(n_sets - 1)]
     outs = [(torch.empty_like(s["q"]),
              torch.empty(s["q"].shape[:2], dtype=torch.float32, device="cuda")) for s in sets]
