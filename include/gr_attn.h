@@ -94,13 +94,17 @@ typedef struct gr_decode_attn_dims {
  * flags; 0 lets the library choose): workgroups of nqt query waves (32
  * stacked query rows each) by nks key streams, with each (request, KV head,
  * query tile) unit's context split over n_split workgroups.  nqt, nks in
- * 1 .. 255, n_split in 1 .. 8; a tiling the library does not compile, or
- * whose LDS does not fit, gives GR_ERR_UNSUPPORTED.  The result is the same
- * (up to rounding order) for every tiling.
+ * 1 .. 255, n_split in 1 .. 8 (1 with GR_FLAG_ROW16); a tiling the library
+ * does not compile, or whose LDS does not fit, gives GR_ERR_UNSUPPORTED.  The
+ * result is the same (up to rounding order) for every tiling.
  */
 #define GR_FLAG_TILING 0x40000000
 #define GR_TILING(nqt, nks, n_split) \
     ((int32_t)(GR_FLAG_TILING | (nqt) | ((nks) << 8) | ((n_split) << 16)))
+/* The same with waves of 16 stacked query rows instead of 32 (more waves per
+ * SIMD for short stacks; no context split across workgroups). */
+#define GR_FLAG_ROW16 0x20000000
+#define GR_TILING16(nqt, nks) ((int32_t)(GR_TILING(nqt, nks, 1) | GR_FLAG_ROW16))
 
 /*
  * Workspace gr_decode_attn / gr_decode_attn_paged need for these sizes, in

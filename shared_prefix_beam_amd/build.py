@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgr_attn.so")
-SOURCES = [os.path.join(CSRC, "gr_attn_kernels.hip"), os.path.join(CSRC, "gr_noalloc.hip"),
+SOURCES = [os.path.join(CSRC, "gr_attn_kernels.hip"), os.path.join(CSRC, "gr_attn16.hip"),
+           os.path.join(CSRC, "gr_noalloc.hip"),
            os.path.join(CSRC, "gr_beam_step.hip"),
            os.path.join(CSRC, "gr_beam_select.hip"), os.path.join(CSRC, "gr_attn_api.cpp")]
 # measurement probes (sustained matrix, HBM and exp2 rates), a library of their own

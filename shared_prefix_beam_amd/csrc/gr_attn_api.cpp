@@ -50,8 +50,9 @@ int validate(const gr_decode_attn_dims *d)
         return GR_ERR_DIMS;
     if (d->flags != 0) {
         const int nqt = d->flags & 255, nks = (d->flags >> 8) & 255, sp = (d->flags >> 16) & 255;
-        if ((d->flags & ~(GR_FLAG_TILING | 0xffffff)) != 0 || !(d->flags & GR_FLAG_TILING) ||
-            nqt < 1 || nks < 1 || sp < 1 || sp > 8)
+        if ((d->flags & ~(GR_FLAG_TILING | GR_FLAG_ROW16 | 0xffffff)) != 0 ||
+            !(d->flags & GR_FLAG_TILING) || nqt < 1 || nks < 1 || sp < 1 || sp > 8 ||
+            ((d->flags & GR_FLAG_ROW16) && sp != 1))
             return GR_ERR_DIMS;
     }
     if (d->Hq % d->Hkv != 0)
@@ -134,6 +135,7 @@ gr::Params make_params(const gr_decode_attn_dims *d, const int32_t *row_offset, 
 // the context is too short for that do wider key streams take over.
 struct Plan {
     int nqt, nks, n_split, n_qt, grid;
+    bool row16 = false;   // waves of 16 stacked rows (gr_attn16.hip)
 };
 
 constexpr int kSIMDs = 256 * 4;
@@ -146,9 +148,9 @@ constexpr int kMaxSplit = 8;              // workgroups per (pair, query tile)
 constexpr int kMinSplitTiles = 4;         // 32-key tiles each split sweeps, at least
 constexpr int kKeyTile = 32;
 
-bool tiling_fits(int D, int nqt, int nks)
+bool tiling_fits(int D, int nqt, int nks, bool row16 = false)
 {
-    const int lds = gr::fused_lds_bytes(D, nqt, nks);
+    const int lds = row16 ? gr::fused16_lds_bytes(D, nqt, nks) : gr::fused_lds_bytes(D, nqt, nks);
     return lds > 0 && lds + kStaticLds <= kLdsBytes;
 }
 
@@ -190,7 +192,8 @@ Plan plan(const gr_decode_attn_dims *d)
         best.nqt = d->flags & 255;
         best.nks = (d->flags >> 8) & 255;
         best.n_split = (d->flags >> 16) & 255;
-        if (!tiling_fits(d->D, best.nqt, best.nks))
+        best.row16 = (d->flags & GR_FLAG_ROW16) != 0;
+        if (!tiling_fits(d->D, best.nqt, best.nks, best.row16))
             best.grid = -2;                     // not compiled or too large
     } else if (o.nqt > 0 && tiling_fits(d->D, o.nqt, o.nks)) {
         best.nqt = o.nqt;
@@ -219,6 +222,7 @@ Plan plan(const gr_decode_attn_dims *d)
                 chosen = true;
             }
         }
+        bool filled = chosen;
         for (const auto &c : cand) {
             if (chosen)
                 break;
@@ -227,13 +231,25 @@ Plan plan(const gr_decode_attn_dims *d)
             best.nqt = c[0];
             best.nks = c[1];
             best.n_split = 1;
-            if (waves(c[0], c[1]) >= want)
+            if (waves(c[0], c[1]) >= want) {
+                filled = true;
                 break;
+            }
+        }
+        // Few stacked rows per pair: waves of 16 rows, two key streams.
+        // Measured at 8 requests x 128 beams (G = 2, 1024 tokens): 24.5 us
+        // against 28.3 us for the (2,2) tiling, and at one request of 4
+        // beams 4.9 us against 8.1 us; where a 32-row tiling fills two waves
+        // per SIMD it is 1.4-1.5 times slower (its LDS reads per row double).
+        if (!filled && tiling_fits(d->D, 4, 2, true)) {
+            best = Plan{4, 2, 1, 0, 0};
+            best.row16 = true;
         }
     }
     if (best.grid == -2)
         return best;
-    best.n_qt = static_cast<int>((M + 32 * best.nqt - 1) / (32 * best.nqt));
+    const int rows = best.row16 ? 16 * best.nqt : 32 * best.nqt;   // stacked rows per workgroup
+    best.n_qt = static_cast<int>((M + rows - 1) / rows);
     const int64_t pairs_per_xcd = (pairs + 7) / 8;
     const int64_t grid = 8 * pairs_per_xcd * best.n_qt * best.n_split;
     best.grid = grid > INT32_MAX ? -1 : static_cast<int>(grid);
@@ -241,6 +257,13 @@ Plan plan(const gr_decode_attn_dims *d)
 }
 
 size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+hipError_t launch_plan(const gr::Params &p, const Plan &pl, void *stream)
+{
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    return pl.row16 ? gr::launch_fused16(p, pl.nqt, pl.nks, pl.grid, s)
+                    : gr::launch_fused(p, pl.nqt, pl.nks, pl.grid, s);
+}
 
 // Workspace layout of a plan: arrival counters, then the wave partials.
 size_t workspace_bytes(const gr_decode_attn_dims *d, const Plan &pl)
@@ -309,8 +332,7 @@ int gr_decode_attn(const gr_decode_attn_dims *d, const int32_t *row_offset, cons
     st = device_ok();
     if (st != GR_OK)
         return st;
-    const hipError_t e =
-        gr::launch_fused(p, pl.nqt, pl.nks, pl.grid, static_cast<hipStream_t>(stream));
+    const hipError_t e = launch_plan(p, pl, stream);
     return e == hipSuccess ? GR_OK : GR_ERR_LAUNCH;
 }
 
@@ -354,8 +376,7 @@ int gr_decode_attn_noalloc(const gr_decode_attn_dims *d, const int32_t *row_offs
         p.ws_count = static_cast<int32_t *>(sp);
         p.ws_part = static_cast<char *>(sp) + gr::NOALLOC_COUNTER_BYTES;
     }
-    const hipError_t e =
-        gr::launch_fused(p, pl.nqt, pl.nks, pl.grid, static_cast<hipStream_t>(stream));
+    const hipError_t e = launch_plan(p, pl, stream);
     return e == hipSuccess ? GR_OK : GR_ERR_LAUNCH;
 }
 
@@ -402,8 +423,7 @@ int gr_decode_attn_paged(const gr_decode_attn_dims *d, const gr_paged_ctx *c,
     st = device_ok();
     if (st != GR_OK)
         return st;
-    const hipError_t e =
-        gr::launch_fused(p, pl.nqt, pl.nks, pl.grid, static_cast<hipStream_t>(stream));
+    const hipError_t e = launch_plan(p, pl, stream);
     return e == hipSuccess ? GR_OK : GR_ERR_LAUNCH;
 }
 

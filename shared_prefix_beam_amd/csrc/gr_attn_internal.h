@@ -109,6 +109,28 @@ constexpr int fused_lds_total(int D, int nqt, int nks, int nbuf)
 {
     return fused_lds_main(D, nqt, nks, nbuf) + FUSED_PTAB_BYTES;
 }
+// The 16-row-wave kernel (gr_attn16.hip): NQT waves of 16 stacked query
+// rows per key stream; its merge slot is a wave's O^T in lane order.
+#define GR_FOR_EACH_FUSED16_CONFIG(X)                                          \
+    X(128, 4, 2, 4, 2) X(128, 8, 1, 4, 4) X(128, 4, 1, 4, 4) X(128, 6, 1, 4, 3)  \
+    X(128, 2, 2, 4, 2) X(64, 4, 2, 4, 2) X(64, 8, 1, 4, 4)
+constexpr int fused16_lds_main(int D, int nqt, int nks, int nbuf)
+{
+    const int stage = nks * nbuf * 2 * FUSED_KT * D * 2;
+    const int merge = (nks - 1) * nqt * (D / 16 + 1) * 64 * 16;
+    return stage > merge ? stage : merge;
+}
+inline int fused16_lds_bytes(int D, int nqt, int nks)
+{
+#define GR_LDS16_CASE(d, a, c, nb, oc)                                                \
+    if (D == d && nqt == a && nks == c)                                               \
+        return fused16_lds_main(d, a, c, nb);
+    GR_FOR_EACH_FUSED16_CONFIG(GR_LDS16_CASE)
+#undef GR_LDS16_CASE
+    return -1;
+}
+hipError_t launch_fused16(const Params &p, int nqt, int nks, int grid, hipStream_t s);
+
 // Dynamic LDS of a compiled (D, NQT, NKS) instantiation, -1 if not compiled.
 inline int fused_lds_bytes(int D, int nqt, int nks)
 {

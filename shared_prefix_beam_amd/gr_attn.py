@@ -26,16 +26,20 @@ GR_ERR_LAUNCH = -5
 GR_ERR_DEVICE = -6
 GR_ERR_WORKSPACE = -7
 GR_FLAG_TILING = 0x40000000
+GR_FLAG_ROW16 = 0x20000000
 
 
 def tiling_flags(tiling) -> int:
-    """dims flags for a forced (nqt, nks[, n_split]) work decomposition
-    (GR_TILING in include/gr_attn.h); None -> 0 (the library plans)."""
+    """dims flags for a forced (nqt, nks[, n_split[, row16]]) work
+    decomposition (GR_TILING / GR_TILING16 in include/gr_attn.h); row16
+    selects waves of 16 stacked rows.  None -> 0 (the library plans)."""
     if tiling is None:
         return 0
     nqt, nks, *rest = tiling
     split = rest[0] if rest else 1
-    return GR_FLAG_TILING | int(nqt) | (int(nks) << 8) | (int(split) << 16)
+    row16 = bool(rest[1]) if len(rest) > 1 else False
+    return GR_FLAG_TILING | (GR_FLAG_ROW16 if row16 else 0) | int(nqt) | (int(nks) << 8) | \
+        (int(split) << 16)
 
 EXPORTS = ("gr_decode_attn_workspace_bytes", "gr_decode_attn", "gr_decode_attn_noalloc",
            "gr_decode_attn_generic", "gr_decode_attn_paged",

@@ -68,6 +68,18 @@ hipError_t launch_fused(const Params &p, int nqt, int nks, int grid, hipStream_t
     return hipSuccess;
 }
 
+// The 16-row-wave grid: one workgroup per (pair, 16*nqt-row tile), no split.
+hipError_t launch_fused16(const Params &p, int nqt, int nks, int grid, hipStream_t)
+{
+    ++g_launches;
+    REQUIRE(grid > 0 && nqt > 0 && nks > 0 && p.n_split == 1);
+    REQUIRE(fused16_lds_bytes(p.D, nqt, nks) > 0);
+    const int64_t pairs = (int64_t)p.B * p.Hkv;
+    REQUIRE((int64_t)grid == 8 * ((pairs + 7) / 8) * p.n_qt);
+    REQUIRE((int64_t)p.n_qt * 16 * nqt >= (int64_t)g_call.W_max * p.G);
+    return hipSuccess;
+}
+
 hipError_t launch_generic(const Params &p, hipStream_t)
 {
     ++g_launches;

@@ -81,6 +81,22 @@ def test_paged_every_tiling(tiling, split):
     assert np.array_equal(out, dense_out) and np.array_equal(lse, dense_lse)
 
 
+TILINGS16 = [(128, 4, 2), (128, 8, 1), (128, 4, 1), (128, 6, 1), (128, 2, 2), (64, 4, 2),
+             (64, 8, 1)]
+
+
+@pytest.mark.parametrize("tiling", TILINGS16, ids=[f"d{d}_q{a}_k{c}" for d, a, c in TILINGS16])
+def test_paged_row16_tilings(tiling):
+    """16-row waves on a paged context: bitwise equal to the dense launch."""
+    D, nqt, nks = tiling
+    inp = ragged(D=D, Hq=16 if D == 128 else 8, Hkv=8 if D == 128 else 4, seed=nqt * 5 + nks)
+    pg = I.to_paged(inp, 16, seed=4)
+    log(f"[paged] row16 tiling {tiling}")
+    out, lse = run_paged(inp, pg, tiling=(nqt, nks, 1, True))
+    dense_out, dense_lse = run_lib(inp, "fused", tiling=(nqt, nks, 1, True))
+    assert np.array_equal(out, dense_out) and np.array_equal(lse, dense_lse)
+
+
 @pytest.mark.parametrize("cfg,page_size", [(2, 16), (4, 64), (3, 32)])
 def test_paged_workloads(cfg, page_size):
     inp = I.generate(I.WORKLOADS[cfg])

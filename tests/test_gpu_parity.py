@@ -112,6 +112,49 @@ def test_every_tiling_ragged(tiling, split):
     assert_parity(out, lse, ref_out, ref_lse, f"tiling {tiling} split {split}")
 
 
+TILINGS16 = [(128, 4, 2), (128, 8, 1), (128, 4, 1), (128, 6, 1), (128, 2, 2), (64, 4, 2),
+             (64, 8, 1)]
+
+
+@pytest.mark.parametrize("tiling", TILINGS16, ids=[f"d{d}_q{a}_k{c}" for d, a, c in TILINGS16])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 8])
+def test_row16_tilings_ragged(tiling, G):
+    """Waves of 16 stacked query rows (the 16x16x32 kernel), each compiled
+    tiling forced per call, on ragged requests with every group size."""
+    D, nqt, nks = tiling
+    Hkv = 8 if G <= 4 else 2
+    inp = I.custom(B=3, Hq=Hkv * G, Hkv=Hkv, D=D, W=[37, 5, 70], ctx_len=[1000, 33, 517],
+                   beam_len=[3, 1, 5], seed=200 + nqt * 10 + nks + 1000 * G)
+    log(f"[parity] row16 D={D} NQT={nqt} NKS={nks} G={G} R={inp.R}")
+    out, lse = run_lib(inp, "fused", tiling=(nqt, nks, 1, True))
+    ref_out, ref_lse = O.decode_attn_inputs(inp)
+    assert_parity(out, lse, ref_out, ref_lse, f"row16 {tiling} G={G}")
+
+
+@pytest.mark.parametrize("cfg,tiling", [(2, (4, 2)), (4, (6, 1)), (4, (8, 1)), (3, (6, 1)),
+                                        (5, (6, 1))])
+def test_row16_workloads(cfg, tiling):
+    """Full workloads through the 16-row kernel: every row against the oracle."""
+    inp = workload(cfg)
+    log(f"[parity] row16 workload {cfg} tiling {tiling}")
+    out, lse = run_lib(inp, "fused", tiling=(tiling[0], tiling[1], 1, True))
+    ref_out, ref_lse = workload_ref(cfg)
+    assert_parity(out, lse, ref_out, ref_lse, f"row16 cfg{cfg} {tiling}")
+
+
+def test_row16_rising_scores_take_exact_sweep():
+    inp = I.custom(B=1, Hq=16, Hkv=8, D=128, W=[40], ctx_len=[600], beam_len=[2], seed=9)
+    k = I.bf16_bits_to_f32(inp.ctx_k).copy()
+    ramp = np.linspace(0.05, 6.0, inp.ctx_cap, dtype=np.float32)[None, :, None, None]
+    inp.ctx_k[:] = I.to_bf16_bits(k * ramp)
+    inp.q[:] = I.to_bf16_bits(I.bf16_bits_to_f32(inp.q) * np.float32(4.0))
+    log("[parity] row16 rising scores (exact re-sweep)")
+    out, lse = run_lib(inp, "fused", tiling=(4, 2, 1, True))
+    ref_out, ref_lse = O.decode_attn_inputs(inp)
+    assert (ref_lse > 60).any()
+    assert_parity(out, lse, ref_out, ref_lse, "row16 rising")
+
+
 def test_split_is_deterministic():
     """The last workgroup of a split unit combines the partials in ascending
     split order whichever workgroup it is: repeated calls are bitwise equal."""
