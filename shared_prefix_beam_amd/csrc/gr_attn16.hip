@@ -23,8 +23,13 @@
 //     (ds_read_b64_tr_b16) of the row-major V tile per 16-row d block.
 //   * Tiles, direct loads, the ring, the fixed-reference softmax with its
 //     exact re-sweep and the merge of key streams are those of the 32-row
-//     kernel.  No context split across workgroups; BeamKV rows are gathered
-//     by each lane with vector loads and folded before the sweep.
+//     kernel.  No context split across workgroups.
+//   * BeamKV rows are gathered by each lane with vector loads and folded
+//     online on the vector units: either by the sweep waves before their
+//     sweep (BW = 0), or (BW = 1) by NQT extra beam waves, one per query
+//     tile, while the sweep waves run the context.  A beam wave takes part
+//     in every barrier of the sweep (it does its gathers and folds between
+//     them), and its partial joins the key streams' in the LDS merge.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,21 +48,28 @@ struct Geo16 {
     static constexpr int OSLOT = (DB + 1) * 64 * 16;      // a wave's O^T + stats, lane order
 };
 
-template <int D, int NQT, int NKS, int NBUF>
+template <int D, int NQT, int NKS, int NBUF, bool BW>
 constexpr int lds16_bytes()
 {
     constexpr int stage = NKS * NBUF * Geo<D>::TILE;
-    constexpr int merge = (NKS - 1) * NQT * Geo16<D>::OSLOT;
-    static_assert((stage > merge ? stage : merge) == fused16_lds_main(D, NQT, NKS, NBUF),
+    constexpr int merge = (NKS - 1 + (BW ? 1 : 0)) * NQT * Geo16<D>::OSLOT;
+    static_assert((stage > merge ? stage : merge) == fused16_lds_main(D, NQT, NKS, NBUF, BW),
                   "host and device LDS layouts differ");
     return stage > merge ? stage : merge;
 }
 
+// sweep barriers a beam wave lets pass between issuing a chunk's BeamKV
+// loads and folding them
+#ifndef BW_SLACK
+#define BW_SLACK 3
+#endif
+
 __device__ __forceinline__ float xor16(float x) { return __shfl_xor(x, 16); }
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
-template <int D, int NQT, int NKS, int NBUF, int OCC, bool PAGED>
-__global__ __launch_bounds__(64 * NQT * NKS) __attribute__((amdgpu_waves_per_eu(OCC)))
+template <int D, int NQT, int NKS, int NBUF, int OCC, bool BW, bool PAGED>
+__global__ __launch_bounds__(64 * (NQT * NKS + (BW ? NQT : 0)))
+__attribute__((amdgpu_waves_per_eu(OCC)))
 void fused_decode_attn16(const Params p)
 {
     using Gm = Geo<D>;
@@ -88,8 +100,11 @@ void fused_decode_attn16(const Params p)
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    const int qt = wave % NQT;
-    const int ks = wave / NQT;
+    // waves 0 .. NQT*NKS-1 sweep the context (query tile qt, key stream
+    // ks); with BW the next NQT waves are the beam waves of the query tiles
+    const bool bwave = BW && wave >= NQT * NKS;
+    const int qt = bwave ? wave - NQT * NKS : wave % NQT;
+    const int ks = bwave ? 0 : wave / NQT;
     const int n = lane & 15;                      // the lane's query within the wave
     const int lg = lane >> 4;                     // the lane's 16-lane group
     const int wrow0 = tile_row0 + qt * WR;
@@ -108,7 +123,7 @@ void fused_decode_attn16(const Params p)
     int pidx0[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const bool on = wave_live && qvalid && u < n_steps;
+        const bool on = !BW && wave_live && qvalid && u < n_steps;
         pidx0[u] = on ? p.beam_path[(int64_t)qrow * p.T_cap + ks + u * NKS] : 0;
     }
     u32x4 qf[G16::DC];
@@ -478,6 +493,32 @@ void fused_decode_attn16(const Params p)
     // Each lane loads its query's rows (K: d = 32c + 8lg .. +8; V: d = 16db +
     // 4lg .. +3) and folds them online into `o`; up to two steps' loads are
     // in flight together.
+    // online fold of one BeamKV step into (m_ref, l_run, l_lse, o); l_run
+    // and l_lse hold the step weights on the lanes of group 0 only
+    auto fold_step = [&](const u32x4 (&kr)[G16::DC], const u32x2 (&vr)[G16::DB])
+        __attribute__((always_inline)) {
+        float dot = 0.f;
+#pragma unroll
+        for (int c = 0; c < G16::DC; ++c)
+            dot = dot8(qf[c], kr[c], dot);
+        dot += xor16(dot);
+        dot += xor32(dot);
+        const float tz = dot * cs;
+        const float mn = __builtin_fmaxf(m_ref, tz);
+        const float alpha = m_ref == NEG_INF ? 0.f : exp2_fast(m_ref - mn);
+        const float pw = exp2_fast(tz - mn);
+        m_ref = mn;
+        l_run = l_run * alpha + (lg == 0 ? pw : 0.f);
+        l_lse = l_lse * alpha + (lg == 0 ? pw : 0.f);
+#pragma unroll
+        for (int db = 0; db < G16::DB; ++db) {
+            const u32x2 v = vr[db];
+            o[db][0] = o[db][0] * alpha + pw * bf16lo(v[0]);
+            o[db][1] = o[db][1] * alpha + pw * bf16hi(v[0]);
+            o[db][2] = o[db][2] * alpha + pw * bf16lo(v[1]);
+            o[db][3] = o[db][3] * alpha + pw * bf16hi(v[1]);
+        }
+    };
     auto beam_stage = [&](bool pre) __attribute__((always_inline)) {
         if (!wave_live)
             return;
@@ -505,40 +546,105 @@ void fused_decode_attn16(const Params p)
             for (int u = 0; u < 2; ++u) {
                 if (i0 + u >= n_steps)
                     break;
-                float dot = 0.f;
-#pragma unroll
-                for (int c = 0; c < G16::DC; ++c)
-                    dot = dot8(qf[c], kr[u][c], dot);
-                dot += xor16(dot);
-                dot += xor32(dot);
-                const float tz = dot * cs;
-                const float mn = __builtin_fmaxf(m_ref, tz);
-                const float alpha = m_ref == NEG_INF ? 0.f : exp2_fast(m_ref - mn);
-                const float pw = exp2_fast(tz - mn);
-                m_ref = mn;
-                l_run = l_run * alpha + (lg == 0 ? pw : 0.f);
-                l_lse = l_lse * alpha + (lg == 0 ? pw : 0.f);
-#pragma unroll
-                for (int db = 0; db < G16::DB; ++db) {
-                    const u32x2 v = vr[u][db];
-                    o[db][0] = o[db][0] * alpha + pw * bf16lo(v[0]);
-                    o[db][1] = o[db][1] * alpha + pw * bf16hi(v[0]);
-                    o[db][2] = o[db][2] * alpha + pw * bf16lo(v[1]);
-                    o[db][3] = o[db][3] * alpha + pw * bf16hi(v[1]);
-                }
+                fold_step(kr[u], vr[u]);
             }
         }
     };
+
+    // ---- beam wave (BW): all BeamKV steps of the query tile's rows --------
+    // BSTEP steps at a time: their BeamKV rows are issued, BW_SLACK of the
+    // sweep's barriers pass while they travel, then they are folded; the
+    // BeamPath entries of the next chunk are fetched a chunk ahead.  It then
+    // takes the rest of the sweep's barriers (and those of an exact
+    // re-sweep), and leaves its partial in its merge slot.
+    auto beam_wave_run = [&]() __attribute__((always_inline)) {
+        constexpr int BSTEP = 3;
+        const int bars = iters + 2;               // barriers of the accumulation sweep
+        int done = 0;
+        auto tick = [&]() __attribute__((always_inline)) {
+            if (done < bars) {
+                block_barrier();
+                ++done;
+            }
+        };
+        const bool on_row = wave_live && qvalid;
+        int qr = qrow;
+        asm volatile("" : "+v"(qr));
+        const int32_t *prow = p.beam_path + (int64_t)qr * p.T_cap;
+        const int64_t req = (int64_t)b * p.beam_cap;
+        int idx_next[BSTEP];
+#pragma unroll
+        for (int u = 0; u < BSTEP; ++u)
+            idx_next[u] = on_row && u < T ? prow[u] : 0;
+        if (T > 0)
+            tick();
+        for (int i0 = 0; i0 < T; i0 += BSTEP) {
+            u32x4 kr[BSTEP][G16::DC];
+            u32x2 vr[BSTEP][G16::DB];
+#pragma unroll
+            for (int u = 0; u < BSTEP; ++u) {
+                const bool on = on_row && i0 + u < T;
+                const int64_t base = ((req + idx_next[u]) * p.Hkv + g) * D;
+#pragma unroll
+                for (int c = 0; c < G16::DC; ++c)
+                    kr[u][c] = on ? ldg16(p.beam_k + base + 32 * c + 8 * lg) : u32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int db = 0; db < G16::DB; ++db)
+                    vr[u][db] = on ? ldg8(p.beam_v + base + 16 * db + 4 * lg) : u32x2{0, 0};
+            }
+#pragma unroll
+            for (int u = 0; u < BSTEP; ++u) {
+                const int st = i0 + BSTEP + u;
+                idx_next[u] = on_row && st < T ? prow[st] : 0;
+            }
+            for (int k = 0; k < BW_SLACK; ++k)
+                tick();
+#pragma unroll
+            for (int u = 0; u < BSTEP; ++u) {
+                if (i0 + u >= T)
+                    break;
+                fold_step(kr[u], vr[u]);
+            }
+        }
+        while (done < bars) {
+            block_barrier();
+            ++done;
+        }
+        if (__syncthreads_or(0)) {                 // the sweep waves sweep again
+            for (int i = 0; i < 2 * iters + 3; ++i)
+                block_barrier();
+        }
+        l_run += xor16(l_run);
+        l_run += xor32(l_run);
+        l_lse += xor16(l_lse);
+        l_lse += xor32(l_lse);
+        if (wave_live) {
+            char *sp = smem + ((NKS - 1) * NQT + qt) * G16::OSLOT;
+#pragma unroll
+            for (int db = 0; db < G16::DB; ++db)
+                *reinterpret_cast<f32x4 *>(sp + (db * 64 + lane) * 16) = o[db];
+            *reinterpret_cast<f32x4 *>(sp + (G16::DB * 64 + lane) * 16) =
+                f32x4{m_ref, l_run, l_lse, 0.f};
+        }
+        __syncthreads();                           // the merge's barrier
+    };
+    if constexpr (BW) {
+        if (bwave) {
+            beam_wave_run();
+            return;
+        }
+    }
 
     // The first tiles' direct loads go out before the beam stage, so that
     // their latency overlaps the BeamPath and BeamKV loads (the beam stage's
     // waits may also wait for them: they were issued first).
     prefetch();
-    beam_stage(true);
+    if constexpr (!BW)
+        beam_stage(true);
     sweep_acc(true, true);
     bool beam_again = false;
     if (__syncthreads_or(qvalid && !(l_lse < SAFE_SUM))) {
-        beam_again = true;                         // the beam partial is dropped with the rest
+        beam_again = !BW;                          // the beam partial is dropped with the rest
         m_ref = NEG_INF;
         l_run = 0.f;
         l_lse = 0.f;
@@ -564,7 +670,7 @@ void fused_decode_attn16(const Params p)
     l_lse += xor32(l_lse);
 
     // ---- merge of the key streams through LDS (log-sum-exp) ---------------
-    if constexpr (NKS > 1) {
+    if constexpr (NKS > 1 || BW) {
         char *ml = smem;                           // the tile ring is free now
         if (ks > 0 && wave_live) {
             char *sp = ml + ((ks - 1) * NQT + qt) * G16::OSLOT;
@@ -577,7 +683,8 @@ void fused_decode_attn16(const Params p)
         __syncthreads();
         if (ks == 0 && wave_live) {
 #pragma unroll
-            for (int k2 = 1; k2 < NKS; ++k2) {
+            // the other key streams' partials, then (BW) the beam wave's
+            for (int k2 = 1; k2 < NKS + (BW ? 1 : 0); ++k2) {
                 const char *sp = ml + ((k2 - 1) * NQT + qt) * G16::OSLOT;
                 const f32x4 st = *reinterpret_cast<const f32x4 *>(sp + (G16::DB * 64 + lane) * 16);
                 const float mo = st[0];
@@ -615,11 +722,11 @@ void fused_decode_attn16(const Params p)
     }
 }
 
-template <int D, int NQT, int NKS, int NBUF, int OCC, bool PAGED>
+template <int D, int NQT, int NKS, int NBUF, int OCC, bool BW, bool PAGED>
 static hipError_t launch_fused16_t(const Params &p, int grid, hipStream_t s)
 {
-    constexpr int lds = lds16_bytes<D, NQT, NKS, NBUF>();
-    auto kern = fused_decode_attn16<D, NQT, NKS, NBUF, OCC, PAGED>;
+    constexpr int lds = lds16_bytes<D, NQT, NKS, NBUF, BW>();
+    auto kern = fused_decode_attn16<D, NQT, NKS, NBUF, OCC, BW, PAGED>;
     // the dynamic-LDS limit is raised once per instantiation and device
     static std::atomic<uint64_t> attr_set{0};
     int dev = 0;
@@ -634,16 +741,16 @@ static hipError_t launch_fused16_t(const Params &p, int grid, hipStream_t s)
             return e;
         attr_set.fetch_or(bit, std::memory_order_release);
     }
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NQT * NKS), lds, s, p);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * (NQT * NKS + (BW ? NQT : 0))), lds, s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_fused16(const Params &p, int nqt, int nks, int grid, hipStream_t s)
 {
-#define GR_LAUNCH16_CASE(d, a, c, nb, oc)                                             \
+#define GR_LAUNCH16_CASE(d, a, c, nb, oc, bw)                                         \
     if (p.D == d && nqt == a && nks == c)                                             \
-        return p.page_table ? launch_fused16_t<d, a, c, nb, oc, true>(p, grid, s)       \
-                            : launch_fused16_t<d, a, c, nb, oc, false>(p, grid, s);
+        return p.page_table ? launch_fused16_t<d, a, c, nb, oc, bw, true>(p, grid, s)   \
+                            : launch_fused16_t<d, a, c, nb, oc, bw, false>(p, grid, s);
     GR_FOR_EACH_FUSED16_CONFIG(GR_LAUNCH16_CASE)
 #undef GR_LAUNCH16_CASE
     return hipErrorInvalidValue;

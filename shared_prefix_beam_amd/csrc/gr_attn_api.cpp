@@ -236,11 +236,12 @@ Plan plan(const gr_decode_attn_dims *d)
                 break;
             }
         }
-        // Few stacked rows per pair: waves of 16 rows, two key streams.
-        // Measured at 8 requests x 128 beams (G = 2, 1024 tokens): 24.5 us
-        // against 28.3 us for the (2,2) tiling, and at one request of 4
-        // beams 4.9 us against 8.1 us; where a 32-row tiling fills two waves
-        // per SIMD it is 1.4-1.5 times slower (its LDS reads per row double).
+        // Few stacked rows per pair: waves of 16 rows, two key streams and
+        // beam waves.  Measured at 8 requests x 128 beams (G = 2, 1024
+        // tokens): 23.2 us against 28.3 us for the (2,2) tiling, and at one
+        // request of 4 beams 5.3 us against 8.1 us; where a 32-row tiling
+        // fills two waves per SIMD it is 1.4-1.5 times slower (its LDS reads
+        // per row double).
         if (!filled && tiling_fits(d->D, 4, 2, true)) {
             best = Plan{4, 2, 1, 0, 0};
             best.row16 = true;

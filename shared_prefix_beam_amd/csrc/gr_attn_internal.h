@@ -111,20 +111,25 @@ constexpr int fused_lds_total(int D, int nqt, int nks, int nbuf)
 }
 // The 16-row-wave kernel (gr_attn16.hip): NQT waves of 16 stacked query
 // rows per key stream; its merge slot is a wave's O^T in lane order.
+// Columns: (head dim, NQT, NKS, NBUF, OCC, BW).  BW = 1 adds NQT beam waves,
+// one per query tile, which fold the BeamKV steps of the tile's rows while
+// the NQT*NKS sweep waves run the context; their partials merge with the
+// key streams' through LDS (one slot per key stream past the first and per
+// beam wave, in the tile ring's space).
 #define GR_FOR_EACH_FUSED16_CONFIG(X)                                          \
-    X(128, 4, 2, 4, 2) X(128, 8, 1, 4, 4) X(128, 4, 1, 4, 4) X(128, 6, 1, 4, 3)  \
-    X(128, 2, 2, 4, 2) X(64, 4, 2, 4, 2) X(64, 8, 1, 4, 4)
-constexpr int fused16_lds_main(int D, int nqt, int nks, int nbuf)
+    X(128, 4, 2, 4, 3, 1) X(128, 8, 1, 4, 4, 0) X(128, 4, 1, 4, 4, 0)             \
+    X(128, 6, 1, 4, 3, 0) X(128, 2, 2, 4, 2, 0) X(64, 4, 2, 4, 3, 1) X(64, 8, 1, 4, 4, 0)
+constexpr int fused16_lds_main(int D, int nqt, int nks, int nbuf, int bw)
 {
     const int stage = nks * nbuf * 2 * FUSED_KT * D * 2;
-    const int merge = (nks - 1) * nqt * (D / 16 + 1) * 64 * 16;
+    const int merge = (nks - 1 + bw) * nqt * (D / 16 + 1) * 64 * 16;
     return stage > merge ? stage : merge;
 }
 inline int fused16_lds_bytes(int D, int nqt, int nks)
 {
-#define GR_LDS16_CASE(d, a, c, nb, oc)                                                \
+#define GR_LDS16_CASE(d, a, c, nb, oc, bw)                                            \
     if (D == d && nqt == a && nks == c)                                               \
-        return fused16_lds_main(d, a, c, nb);
+        return fused16_lds_main(d, a, c, nb, bw);
     GR_FOR_EACH_FUSED16_CONFIG(GR_LDS16_CASE)
 #undef GR_LDS16_CASE
     return -1;
