@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gr_attn_internal.h"
 
 namespace gr {
@@ -54,12 +56,6 @@ __device__ __forceinline__ uint64_t make_key(uint32_t ord, uint32_t flat)
     return ((uint64_t)ord << 32) | (uint32_t)~flat;
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m)
-{
-    const uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
-    return ((uint64_t)hi << 32) | lo;
-}
-
 // Value of lane (lane ^ J) for J in {1, 2, 4, 8}, through DPP moves (VALU,
 // no LDS traffic): quad permutations for 1 and 2; for 4 and 8 a row shift
 // up (lane + J) or down (lane - J), picked by the lane's bit J.
@@ -85,6 +81,73 @@ __device__ __forceinline__ uint64_t dpp_xor_u64(uint64_t v)
     return ((uint64_t)hi << 32) | lo;
 }
 
+// Value of lane (lane ^ J) for any power of two J < 64 without LDS traffic:
+// the DPP moves above for J <= 8; for 16 and 32 one v_permlane16_swap /
+// v_permlane32_swap with both operands equal to v (it exchanges the odd
+// 16-lane rows, resp. the upper half, of its first operand with the even
+// rows, resp. the lower half, of its second: a lane finds its partner's
+// value in the first result when its bit J is set, else in the second).
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v)
+{
+    if constexpr (J <= 8) {
+        return dpp_xor_u32<J>(v);
+    } else if constexpr (J == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (threadIdx.x & 16) ? (uint32_t)r[0] : (uint32_t)r[1];
+    } else {
+        static_assert(J == 32, "lane distance");
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (threadIdx.x & 32) ? (uint32_t)r[0] : (uint32_t)r[1];
+    }
+}
+
+template <int J>
+__device__ __forceinline__ uint64_t lane_xor_u64(uint64_t v)
+{
+    const uint32_t lo = lane_xor_u32<J>((uint32_t)v), hi = lane_xor_u32<J>((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Butterfly over the wave: every lane ends with op over all 64 lanes.
+template <class T, class Op>
+__device__ __forceinline__ T wave_allreduce(T v, Op op)
+{
+    auto x = [](T a, auto tag) -> T {
+        constexpr int J = decltype(tag)::value;
+        if constexpr (sizeof(T) == 8) {
+            return __builtin_bit_cast(T, lane_xor_u64<J>(__builtin_bit_cast(uint64_t, a)));
+        } else {
+            return __builtin_bit_cast(T, lane_xor_u32<J>(__builtin_bit_cast(uint32_t, a)));
+        }
+    };
+    v = op(v, x(v, std::integral_constant<int, 32>{}));
+    v = op(v, x(v, std::integral_constant<int, 16>{}));
+    v = op(v, x(v, std::integral_constant<int, 8>{}));
+    v = op(v, x(v, std::integral_constant<int, 4>{}));
+    v = op(v, x(v, std::integral_constant<int, 2>{}));
+    v = op(v, x(v, std::integral_constant<int, 1>{}));
+    return v;
+}
+
+// Inclusive prefix sum over the lanes in order, with DPP: shifts by 1, 2, 4
+// and 8 lanes inside each 16-lane row (a lane with no source adds 0), then
+// the last lane of rows 0 and 2 broadcast into rows 1 and 3, then lane 31
+// into rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31
+    return v;
+}
+
+// Value of a wave-uniform lane `src`.
+__device__ __forceinline__ int lane_value(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
+
 // Largest and smallest 64-bit key over the block (every thread passes its
 // own; threads with no key pass kmax = 0, kmin = ~0).  One barrier; `red`
 // may be written again only after a later barrier.
@@ -92,11 +155,8 @@ template <int NT>
 __device__ void block_minmax(uint64_t &kmax, uint64_t &kmin, uint64_t *red)
 {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    for (int off = 32; off > 0; off >>= 1) {
-        const uint64_t a = shfl_xor_u64(kmax, off), c = shfl_xor_u64(kmin, off);
-        kmax = a > kmax ? a : kmax;
-        kmin = c < kmin ? c : kmin;
-    }
+    kmax = wave_allreduce(kmax, [](uint64_t a, uint64_t c) { return a > c ? a : c; });
+    kmin = wave_allreduce(kmin, [](uint64_t a, uint64_t c) { return a < c ? a : c; });
     if (lane == 0) {
         red[2 * wv] = kmax;
         red[2 * wv + 1] = kmin;
@@ -116,8 +176,7 @@ template <int NT>
 __device__ int block_sum(int v, int *red)
 {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    for (int off = 32; off > 0; off >>= 1)
-        v += __shfl_xor(v, off);
+    v = wave_allreduce(v, [](int a, int c) { return a + c; });
     if (lane == 0)
         red[wv] = v;
     __syncthreads();
@@ -134,12 +193,7 @@ template <int NT>
 __device__ int block_incl_scan(int v, int *wsum, int &total)
 {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(v, off);
-        if (lane >= off)
-            v += t;
-    }
+    v = wave_incl_scan(v);
     if (lane == 63)
         wsum[wv] = v;
     __syncthreads();
@@ -152,6 +206,43 @@ __device__ int block_incl_scan(int v, int *wsum, int &total)
         total += s;
     }
     return v + before;
+}
+
+// In a complete 256-bin histogram h (published by a barrier), the digit d
+// where the count from the top digit down reaches `remaining`, the count
+// above d and d's own count; every lane of every wave gets the same three.
+// Lane l holds bins 4l .. 4l+3; suffix sums over the lanes find the lane.
+__device__ __forceinline__ void hist_find(const uint32_t *h, int remaining, int &d, int &above,
+                                          int &cnt)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        b[j] = h[4 * lane + j];
+    const uint32_t own = b[0] + b[1] + b[2] + b[3];
+    // suffix sum over the lanes: the total less the prefix before this lane
+    const int incl = wave_incl_scan((int)own);
+    const uint32_t suf = (uint32_t)(lane_value(incl, 63) - incl) + own;
+    const uint32_t above_lane = suf - own;
+    const bool here = suf >= (uint32_t)remaining && above_lane < (uint32_t)remaining;
+    int d_l = 0, above_l = 0, cnt_l = 0;
+    if (here) {
+        uint32_t cum = above_lane;
+        for (int j = 3; j >= 0; --j) {
+            if (cum + b[j] >= (uint32_t)remaining || j == 0) {
+                d_l = 4 * lane + j;
+                above_l = (int)cum;
+                cnt_l = (int)b[j];
+                break;
+            }
+            cum += b[j];
+        }
+    }
+    const int src = __ffsll((unsigned long long)__ballot(here)) - 1;
+    d = lane_value(d_l, src);
+    above = lane_value(above_l, src);
+    cnt = lane_value(cnt_l, src);
 }
 
 // Threshold of the k-th largest of n distinct keys lying in [kmin, kmax], as
@@ -189,37 +280,8 @@ __device__ void radix_kth(int k, uint64_t kmax, uint64_t kmin, Visit visit, uint
                 atomicAdd(&h[(uint32_t)(key >> lo) & dmask], 1u);
         });
         __syncthreads();
-        // lane l holds bins 4l .. 4l+3; suffix sums over lanes find the bin
-        // where the count from the top reaches `remaining`
-        uint32_t b[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            b[j] = h[4 * lane + j];
-        const uint32_t own = b[0] + b[1] + b[2] + b[3];
-        uint32_t suf = own;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t t = __shfl_down(suf, off);
-            if (lane + off < 64)
-                suf += t;
-        }
-        const uint32_t above_lane = suf - own;
-        const bool here = suf >= (uint32_t)remaining && above_lane < (uint32_t)remaining;
-        int d_l = 0, above_l = 0, cnt_l = 0;
-        if (here) {
-            uint32_t cum = above_lane;
-            for (int j = 3; j >= 0; --j) {
-                if (cum + b[j] >= (uint32_t)remaining || j == 0) {
-                    d_l = 4 * lane + j;
-                    above_l = (int)cum;
-                    cnt_l = (int)b[j];
-                    break;
-                }
-                cum += b[j];
-            }
-        }
-        const int src = __ffsll((unsigned long long)__ballot(here)) - 1;
-        const int d = __shfl(d_l, src), above = __shfl(above_l, src), cnt = __shfl(cnt_l, src);
+        int d, above, cnt;
+        hist_find(h, remaining, d, above, cnt);
         prefix |= (uint64_t)d << lo;
         mask |= (uint64_t)dmask << lo;
         remaining -= above;
@@ -243,7 +305,7 @@ __device__ __forceinline__ int wave_append(bool take, int *counter)
     if (ballot) {
         if (lane == leader)
             base = atomicAdd(counter, __popcll(ballot));
-        base = __shfl(base, leader);
+        base = lane_value(base, leader);
     }
     return base + __popcll(ballot & ((1ull << lane) - 1ull));
 }
@@ -269,7 +331,7 @@ __device__ __forceinline__ void bitonic_stage(uint64_t &key, uint64_t *xch2, int
     } else if constexpr (J <= 8) {
         other = dpp_xor_u64<J>(key);
     } else {
-        other = shfl_xor_u64(key, J);
+        other = lane_xor_u64<J>(key);
     }
     const bool same = ((tid & J) == 0) == ((tid & K) == 0);
     key = ((other > key) == same) ? other : key;
@@ -398,8 +460,7 @@ __attribute__((amdgpu_waves_per_eu(NV <= 32 ? 5 : 2))) void select_rows(const Se
 #pragma unroll
     for (int i = 1; i < NV; ++i)
         m = __builtin_fmaxf(m, x[i]);
-    for (int off = 32; off > 0; off >>= 1)
-        m = __builtin_fmaxf(m, __shfl_xor(m, off));
+    m = wave_allreduce(m, [](float a, float c) { return __builtin_fmaxf(a, c); });
     if (lane == 0)
         red[wv] = m;
     __syncthreads();
@@ -412,8 +473,7 @@ __attribute__((amdgpu_waves_per_eu(NV <= 32 ? 5 : 2))) void select_rows(const Se
 #pragma unroll
     for (int i = 0; i < NV; ++i)
         s += __expf(x[i] - m);
-    for (int off = 32; off > 0; off >>= 1)
-        s += __shfl_xor(s, off);
+    s = wave_allreduce(s, [](float a, float c) { return a + c; });
     if (lane == 0)
         red[wv] = s;
     __syncthreads();
@@ -532,34 +592,17 @@ __attribute__((amdgpu_waves_per_eu(NV <= 32 ? 5 : 2))) void select_rows(const Se
 
 __device__ __forceinline__ float wave_max(float v)
 {
-    for (int off = 32; off > 0; off >>= 1)
-        v = __builtin_fmaxf(v, __shfl_xor(v, off));
-    return v;
+    return wave_allreduce(v, [](float a, float c) { return __builtin_fmaxf(a, c); });
 }
 
 __device__ __forceinline__ float wave_sum(float v)
 {
-    for (int off = 32; off > 0; off >>= 1)
-        v += __shfl_xor(v, off);
-    return v;
+    return wave_allreduce(v, [](float a, float c) { return a + c; });
 }
 
 __device__ __forceinline__ int wave_sum_i(int v)
 {
-    for (int off = 32; off > 0; off >>= 1)
-        v += __shfl_xor(v, off);
-    return v;
-}
-
-__device__ __forceinline__ int wave_incl_scan(int v, int lane)
-{
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(v, off);
-        if (lane >= off)
-            v += t;
-    }
-    return v;
+    return wave_allreduce(v, [](int a, int c) { return a + c; });
 }
 
 // One beam row per wave, four rows per 256-thread workgroup, no block
@@ -668,8 +711,8 @@ __global__ __launch_bounds__(256) void select_rows_wave(const SelParams p)
         for (int i = 0; i < NL; ++i)
             c += ord_at(i, ow) >= res ? 1 : 0;
     }
-    int incl = wave_incl_scan(c, lane);
-    int M = __shfl(incl, 63);
+    int incl = wave_incl_scan(c);
+    int M = lane_value(incl, 63);
     int n_keys = 0;                               // keys placed in cand
     if (M <= SEL_WCAND) {
         int at = incl - c;
@@ -702,8 +745,8 @@ __global__ __launch_bounds__(256) void select_rows_wave(const SelParams p)
             for (int i = 0; i < NL; ++i)
                 c += ord_at(i, ow) > acc ? 1 : 0;
         }
-        incl = wave_incl_scan(c, lane);
-        const int A = __shfl(incl, 63);           // < L
+        incl = wave_incl_scan(c);
+        const int A = lane_value(incl, 63);       // < L
         int at = incl - c;
         const Pass ow = fresh();
 #pragma unroll
@@ -857,7 +900,11 @@ __global__ __launch_bounds__(SEL_REQ_THREADS) void select_request(const SelParam
         // keys are >= pf, so pf bounds the request's K_eff-th best
         // candidate from below.  (One LDS histogram pass per 8-bit digit;
         // measured much cheaper than a bit-by-bit ballot search of each
-        // wave's share, and exact, so fewer candidates survive the cut.)
+        // wave's share, and exact, so fewer candidates survive the cut.
+        // A first pass over equal-width value bins instead of the exponent
+        // digit was measured no faster: the first pass costs its LDS
+        // atomics, about one key per clock per compute unit, however the
+        // keys spread.)
         uint64_t kmax = 0, kmin = ~0ull;
         visit([&](uint64_t key) {
             kmax = key > kmax ? key : kmax;
