@@ -40,6 +40,9 @@ MALL_BYTES = 256 << 20
 PRIMARY = 2                   # Qwen3-0.6B shape, W=128
 SECONDARY = 4                 # Qwen3-0.6B shape, W=900
 KERNEL_SOURCES = ["shared_prefix_beam_amd/csrc/gr_attn_kernels.hip",
+                  "shared_prefix_beam_amd/csrc/gr_attn16.hip",
+                  "shared_prefix_beam_amd/csrc/gr_attn_device.h",
+                  "shared_prefix_beam_amd/csrc/gr_attn_internal.h",
                   "shared_prefix_beam_amd/csrc/gr_attn_api.cpp"]
 STEP_SOURCES = ["shared_prefix_beam_amd/csrc/gr_beam_step.hip"]
 STEP_CFGS = (4, 2)            # beam-step shapes reported (900 and 128 beams)
@@ -201,7 +204,8 @@ def write_profile_summaries(d: str):
         inp = I.generate(wl)
         nbytes, flops = algorithmic(inp)
         kern = [r for r in stats if "fused_decode_attn" in r["Name"]]
-        lines = [f"# fused_decode_attn on {wl.name}", "",
+        kname = kern[0]["Name"] if kern else "fused_decode_attn"
+        lines = [f"# fused decode attention on {wl.name}", "", f"kernel: {kname}", "",
                  "kernel trace (rocprofv3 --kernel-trace --stats), command from the repository root:",
                  "    " + PROFILE_COMMANDS["trace"].format(d="gpurun_out/prof", w=which), "",
                  f"{'kernel':60s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
@@ -230,7 +234,7 @@ def write_profile_summaries(d: str):
                   f"kernel sources sha256[:16] {sha}"]
         name = f"fused_decode_attn_{wl.name}"
         open(os.path.join(out_dir, name + ".txt"), "w").write("\n".join(lines) + "\n")
-        json.dump({"kernel": "fused_decode_attn", "workload": wl.name, "kernel_sha": sha,
+        json.dump({"kernel": kname, "workload": wl.name, "kernel_sha": sha,
                    "bytes_per_launch": traffic, "fetch_kib": fetch_kib, "write_kib": write_kib,
                    "fetch_factor": f_fetch, "write_factor": f_write, "avg_launch_us": avg_us},
                   open(os.path.join(out_dir, f"traffic_{name}.json"), "w"), indent=1)
@@ -397,6 +401,7 @@ def measure(cfg: int, steps: int, warmup: int, page_size=None, reps: int = 5,
                         beam_cap=inp.beam_cap, scale=0.0, flags=0)
     workspace = gr_attn.attach_workspace(dims, None, "cuda")
     ws_bytes = int(dims.workspace_bytes)
+    plan = gr_attn.plan(dims)
 
     # one front-end call per input copy validates shapes; the timed loop then
     # calls the C entry point directly with the same arguments
@@ -491,10 +496,15 @@ def measure(cfg: int, steps: int, warmup: int, page_size=None, reps: int = 5,
                 launch_ms=launch[0], launch_median_ms=srt[len(srt) // 2], launch_min_ms=srt[0],
                 launch_reps_ms=launch, latency_ms=sorted(lat)[len(lat) // 2] if lat else None,
                 n_sets=n_sets, spot_abs=spot, spot_lse=spot_lse, spot_rows=len(rows),
-                workspace_bytes=ws_bytes)
+                workspace_bytes=ws_bytes, plan=plan)
 
 
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop per byte
+
+
+def kernel_of(plan: dict) -> str:
+    """The fused kernel a plan launches."""
+    return "fused_decode_attn16" if plan["row16"] else "fused_decode_attn"
 
 
 def config_entry(cfg: int, r) -> dict:
@@ -514,6 +524,7 @@ def config_entry(cfg: int, r) -> dict:
             "TFLOPs": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS,
             "bound": "hbm" if ai < RIDGE else "mfma", "flop_per_byte": ai,
             "algorithmic_bytes": r["nbytes"], "algorithmic_flops": r["flops"],
+            "kernel": kernel_of(r["plan"]), "plan": r["plan"],
             "workspace_bytes": r["workspace_bytes"], "traffic": recorded_traffic(inp.wl.name),
             "spot_check": {"rows": r["spot_rows"], "max_abs": r["spot_abs"],
                            "lse_abs": r["spot_lse"]}}
@@ -898,7 +909,8 @@ def main():
                    "input_copies_rotated": prim["n_sets"]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel": "fused_decode_attn", "launch_us": prim["launch_ms"] * 1e3,
+                     "kernel": kernel_of(prim["plan"]), "plan": prim["plan"],
+                     "launch_us": prim["launch_ms"] * 1e3,
                      "launch_us_median": prim["launch_median_ms"] * 1e3,
                      "launch_us_min": prim["launch_min_ms"] * 1e3,
                      "algorithmic_bytes": prim["nbytes"]},
@@ -915,6 +927,7 @@ def main():
             "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
                          "traffic": recorded_traffic(si.wl.name),
+                         "kernel": kernel_of(sec["plan"]), "plan": sec["plan"],
                          "launch_us": sec["launch_ms"] * 1e3,
                          "launch_us_median": sec["launch_median_ms"] * 1e3,
                          "launch_us_min": sec["launch_min_ms"] * 1e3,

@@ -129,6 +129,18 @@ typedef struct gr_decode_attn_dims {
 size_t gr_decode_attn_workspace_bytes(const gr_decode_attn_dims *dims);
 
 /*
+ * The work decomposition gr_decode_attn / gr_decode_attn_paged plan for these
+ * dims, by the same rules (for reporting and tuning; the pages leave the
+ * decomposition to the implementation).  On GR_OK, plan (host memory, 5
+ * int32) holds: [0] nqt, [1] nks, [2] n_split, [3] 1 for waves of 16 stacked
+ * query rows (0: 32), [4] the launch's workgroup count (all 0 when the call
+ * has nothing to compute).  Errors as gr_decode_attn for invalid dims
+ * (GR_ERR_NULL also for a NULL plan; GR_ERR_UNSUPPORTED for a forced tiling
+ * the library does not compile); no device is touched.
+ */
+int gr_decode_attn_plan(const gr_decode_attn_dims *dims, int32_t plan[5]);
+
+/*
  * Large-beam decode attention (shared ContextKV stage on bf16 MFMA with an
  * online softmax, per-beam BeamPath gather, log-sum-exp merge), one launch
  * on `stream`.  row_offset is a DEVICE pointer to int32[B+1]; it is a

@@ -305,6 +305,28 @@ size_t gr_decode_attn_workspace_bytes(const gr_decode_attn_dims *d)
     return workspace_bytes(d, plan(d));
 }
 
+int gr_decode_attn_plan(const gr_decode_attn_dims *d, int32_t plan_out[5])
+{
+    if (!plan_out)
+        return GR_ERR_NULL;
+    const int st = validate(d);
+    if (st != GR_OK)
+        return st;
+    for (int i = 0; i < 5; ++i)
+        plan_out[i] = 0;
+    if (d->R == 0 || d->B == 0 || d->W_max == 0)
+        return GR_OK;
+    const Plan pl = plan(d);
+    if (pl.grid < 0)
+        return pl.grid == -2 ? GR_ERR_UNSUPPORTED : GR_ERR_DIMS;
+    plan_out[0] = pl.nqt;
+    plan_out[1] = pl.nks;
+    plan_out[2] = pl.n_split;
+    plan_out[3] = pl.row16 ? 1 : 0;
+    plan_out[4] = pl.grid;
+    return GR_OK;
+}
+
 int gr_decode_attn(const gr_decode_attn_dims *d, const int32_t *row_offset, const void *q,
                    const void *ctx_k, const void *ctx_v, const int32_t *ctx_len,
                    const void *beam_k, const void *beam_v, const int32_t *beam_path,

@@ -41,7 +41,8 @@ def tiling_flags(tiling) -> int:
     return GR_FLAG_TILING | (GR_FLAG_ROW16 if row16 else 0) | int(nqt) | (int(nks) << 8) | \
         (int(split) << 16)
 
-EXPORTS = ("gr_decode_attn_workspace_bytes", "gr_decode_attn", "gr_decode_attn_noalloc",
+EXPORTS = ("gr_decode_attn_workspace_bytes", "gr_decode_attn_plan", "gr_decode_attn",
+           "gr_decode_attn_noalloc",
            "gr_decode_attn_generic", "gr_decode_attn_paged",
            "gr_check_metadata", "gr_beam_step", "gr_beam_select_workspace_bytes",
            "gr_beam_select", "gr_beam_select_trie", "gr_status_str", "gr_version")
@@ -117,6 +118,8 @@ def load() -> ctypes.CDLL:
             fn.restype = ctypes.c_int
         lib.gr_decode_attn_workspace_bytes.argtypes = [DP]
         lib.gr_decode_attn_workspace_bytes.restype = ctypes.c_size_t
+        lib.gr_decode_attn_plan.argtypes = [DP, ctypes.POINTER(ctypes.c_int32)]
+        lib.gr_decode_attn_plan.restype = ctypes.c_int
         lib.gr_check_metadata.argtypes = [DP, P, P, P, P, P, P]
         lib.gr_check_metadata.restype = ctypes.c_int
         lib.gr_decode_attn_paged.argtypes = [DP, ctypes.POINTER(PagedCtx)] + [P] * 10
@@ -232,6 +235,16 @@ def make_dims(q, ctx_k, beam_k, beam_path, W_max: int, scale: Optional[float] = 
     return Dims(B=B, R=R, Hq=Hq, Hkv=Hkv, D=D, W_max=int(W_max), T_cap=beam_path.shape[1],
                 reserved=0, ctx_cap=ctx_cap, beam_cap=beam_k.shape[1],
                 scale=0.0 if scale is None else float(scale), flags=tiling_flags(tiling))
+
+
+def plan(dims: Dims) -> dict:
+    """The work decomposition the library plans for ``dims``
+    (gr_decode_attn_plan): nqt, nks, n_split, row16, grid."""
+    out = (ctypes.c_int32 * 5)()
+    st = load().gr_decode_attn_plan(ctypes.byref(dims), out)
+    if st != GR_OK:
+        raise GrAttnError(st, "gr_decode_attn_plan")
+    return dict(nqt=out[0], nks=out[1], n_split=out[2], row16=bool(out[3]), grid=out[4])
 
 
 def attach_workspace(dims: Dims, workspace, device):

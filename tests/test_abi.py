@@ -122,6 +122,46 @@ def test_workspace_bytes():
         assert n == want, (nqt, nks, sp, n, want)
 
 
+def workload_dims(cfg):
+    from shared_prefix_beam_amd import inputs as I
+    wl = I.WORKLOADS[cfg]
+    return gr_attn.Dims(B=wl.B, R=sum(wl.W), Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D, W_max=max(wl.W),
+                        T_cap=wl.T[-1], reserved=0, ctx_cap=wl.ctx[-1], beam_cap=16,
+                        scale=0.0, flags=0)
+
+
+# (nqt, nks, n_split, row16) the planner takes for the five workloads: waves
+# of 16 rows with two key streams where no 32-row tiling fills two waves per
+# SIMD (1 request of 4 beams, 8 requests of 128), else (4,1) of 32-row waves
+@pytest.mark.parametrize("cfg,want", [(1, (4, 2, 1, 1)), (2, (4, 2, 1, 1)), (3, (4, 1, 1, 0)),
+                                      (4, (4, 1, 1, 0)), (5, (4, 1, 1, 0))])
+def test_planner_choices(cfg, want):
+    p = gr_attn.plan(workload_dims(cfg))
+    assert (p["nqt"], p["nks"], p["n_split"], int(p["row16"])) == want
+    d = workload_dims(cfg)
+    pairs = d.B * d.Hkv
+    rows = (16 if p["row16"] else 32) * p["nqt"]
+    n_qt = -(-(d.W_max * (d.Hq // d.Hkv)) // rows)
+    assert p["grid"] == 8 * -(-pairs // 8) * n_qt * p["n_split"]
+
+
+def test_plan_echoes_forced_tilings_and_rejects_bad_ones(lib):
+    p = gr_attn.plan(good_dims(flags=gr_attn.tiling_flags((4, 2, 1, True))))
+    assert (p["nqt"], p["nks"], p["n_split"], p["row16"]) == (4, 2, 1, True)
+    p = gr_attn.plan(split_dims(flags=gr_attn.tiling_flags((4, 1, 4))))
+    assert (p["nqt"], p["nks"], p["n_split"], p["row16"]) == (4, 1, 4, False)
+    p = gr_attn.plan(split_dims())
+    assert p["n_split"] > 1                      # few pairs, long context: split
+    assert gr_attn.plan(good_dims(R=0, W_max=0))["grid"] == 0
+    out = (ctypes.c_int32 * 5)()
+    assert lib.gr_decode_attn_plan(ctypes.byref(good_dims()), None) == gr_attn.GR_ERR_NULL
+    assert lib.gr_decode_attn_plan(None, out) == gr_attn.GR_ERR_NULL
+    assert lib.gr_decode_attn_plan(ctypes.byref(good_dims(Hq=12)), out) == gr_attn.GR_ERR_DIMS
+    st = lib.gr_decode_attn_plan(ctypes.byref(good_dims(flags=gr_attn.tiling_flags((3, 3, 1)))),
+                                 out)
+    assert st == gr_attn.GR_ERR_UNSUPPORTED
+
+
 def test_workspace_rejected():
     need = gr_attn.gr_decode_attn_workspace_bytes(split_dims())
     assert call(split_dims()) == gr_attn.GR_ERR_WORKSPACE                     # NULL
