@@ -48,6 +48,23 @@ struct Geo16 {
     static constexpr int OSLOT = (DB + 1) * 64 * 16;      // a wave's O^T + stats, lane order
 };
 
+// Chunk swizzles of this kernel's K and V tile rows (16-byte chunk c of row
+// r sits in slot c ^ swz(r)), chosen for its own fragment reads: the K read
+// has the 16 lanes of a group on rows 0..15, the V^T read has lane groups
+// lg and lg+1 on rows four apart.  A row spans all 64 four-byte banks at D
+// = 128 and half of them at D = 64; with these swizzles no two lanes of one
+// LDS pass (16 lanes of a 16-byte read, 32 of an 8-byte read) share a bank.
+template <int D>
+__device__ __forceinline__ constexpr int kswz16(int r)
+{
+    return (D == 64 ? r >> 1 : r) & (Geo<D>::CH - 1);
+}
+template <int D>
+__device__ __forceinline__ constexpr int vswz16(int r)
+{
+    return (D == 64 ? r : 2 * r) & (Geo<D>::CH - 1);
+}
+
 template <int D, int NQT, int NKS, int NBUF, bool BW>
 constexpr int lds16_bytes()
 {
@@ -178,7 +195,7 @@ void fused_decode_attn16(const Params p)
         const bool is_v = u >= Gm::LOADS / 2;
         const int uu = is_v ? u - Gm::LOADS / 2 : u;
         const int r = uu * RPL + lane / Gm::CH;
-        const int c = (lane % Gm::CH) ^ (is_v ? vswz<D>(r) : kswz<D>(r));
+        const int c = (lane % Gm::CH) ^ (is_v ? vswz16<D>(r) : kswz16<D>(r));
         loff[i] = (uint32_t)(r * kv_tok + 8 * c) * 2u;
     }
     constexpr bool EVEN = Gm::LOADS % NQT == 0;
@@ -207,7 +224,7 @@ void fused_decode_attn16(const Params p)
                     const bool is_v = u >= Gm::LOADS / 2;
                     const int uu = is_v ? u - Gm::LOADS / 2 : u;
                     const int r = uu * RPL + lane / Gm::CH;
-                    const int c = (lane % Gm::CH) ^ (is_v ? vswz<D>(r) : kswz<D>(r));
+                    const int c = (lane % Gm::CH) ^ (is_v ? vswz16<D>(r) : kswz16<D>(r));
                     const int tok = key0 + r < L ? key0 + r : L - 1;
                     int pg = ptab[tok / p.page_size];
                     pg = pg < 0 ? 0 : (pg >= p.n_pages ? (int)(p.n_pages - 1) : pg);
@@ -272,7 +289,7 @@ void fused_decode_attn16(const Params p)
     uint32_t koff[G16::DC];
 #pragma unroll
     for (int c = 0; c < G16::DC; ++c)
-        koff[c] = stream_off + n * Gm::ROW + 16 * ((4 * c + lg) ^ kswz<D>(n));
+        koff[c] = stream_off + n * Gm::ROW + 16 * ((4 * c + lg) ^ kswz16<D>(n));
     // V^T: in a transposing read, lane a of a 16-lane group receives element
     // a % 4 of the words addressed by lanes a/4 + 4j (j < 4); lane a here
     // addresses row 4lg + a/4, columns 16db + 4(a % 4) .. +3, so lane a
@@ -284,7 +301,7 @@ void fused_decode_attn16(const Params p)
 #pragma unroll
         for (int db = 0; db < G16::DB; ++db)
             voff[db] = stream_off + Gm::KBYTES + vrow * Gm::ROW +
-                       16 * ((2 * db + ((n & 3) >> 1)) ^ vswz<D>(vrow)) + 8 * (n & 1);
+                       16 * ((2 * db + ((n & 3) >> 1)) ^ vswz16<D>(vrow)) + 8 * (n & 1);
     }
 
     auto kread = [&](int buf, u32x4 (&kf)[2][G16::DC]) __attribute__((always_inline)) {
