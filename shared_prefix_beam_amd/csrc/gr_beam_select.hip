@@ -446,148 +446,161 @@ __attribute__((amdgpu_waves_per_eu(NV <= 32 ? 5 : 2))) void select_rows(const Se
     }
 
     const float *row = p.logits + (int64_t)r * p.V;
-    float x[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int v = tid + NT * i;
-        int t = v;
-        if (TRIE && v < n)
-            t = p.edge_tok[e0 + v];
-        x[i] = (v < n && t >= 0 && t < p.V) ? row[t] : -__builtin_huge_valf();
-    }
-    // max and log-sum-exp over the row
-    float m = x[0];
-#pragma unroll
-    for (int i = 1; i < NV; ++i)
-        m = __builtin_fmaxf(m, x[i]);
-    m = wave_allreduce(m, [](float a, float c) { return __builtin_fmaxf(a, c); });
-    if (lane == 0)
-        red[wv] = m;
-    __syncthreads();
-    m = red[0];
-#pragma unroll
-    for (int w = 1; w < NW; ++w)
-        m = __builtin_fmaxf(m, red[w]);
-    __syncthreads();
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-        s += __expf(x[i] - m);
-    s = wave_allreduce(s, [](float a, float c) { return a + c; });
-    if (lane == 0)
-        red[wv] = s;
-    __syncthreads();
-    s = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w)
-        s += red[w];
-    const float off_w = p.score_old[r] - (m + __logf(s));
-    if (tid == 0)
-        p.ws_off[r] = off_w;
-
-    // the candidates' ordered value bits replace the logits
-    uint32_t o[NV];
     const uint32_t flat0 = (uint32_t)wl * (uint32_t)p.V + (uint32_t)tid;
-    const bool has = tid < n;
-    uint64_t tmax = 0;
+    // The body, for rows whose NV*NT candidate slots are all taken (every
+    // unconstrained row of an NV*NT vocabulary: no per-slot validity test
+    // at all) and for the others.  Validity and key comparisons are kept to
+    // 32 bits where the 64-bit keys allow it: every bound below has zero
+    // index bits, so key >= bound is value bits >= the bound's value bits.
+    auto run = [&](auto full_tag) __attribute__((always_inline)) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        auto valid = [&](int i) { return FULL || tid + NT * i < n; };
+        float x[NV];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        o[i] = ord_f32(off_w + x[i]);
-        if (tid + NT * i < n) {
-            const uint64_t key = make_key(o[i], flat0 + NT * i);
-            tmax = key > tmax ? key : tmax;
+        for (int i = 0; i < NV; ++i) {
+            const int v = tid + NT * i;
+            int t = v;
+            if (TRIE && valid(i))
+                t = p.edge_tok[e0 + v];
+            x[i] = (valid(i) && t >= 0 && t < p.V) ? row[t] : -__builtin_huge_valf();
         }
-    }
-    // t0: when every thread holds keys (V >= NT), each wave's q-th best
-    // thread maximum value (q = ceil(L / NW)), found bit by bit with ballots
-    // over the 32 value bits of the keys: at least q distinct keys of the
-    // wave have that value or more, so the key with that value and the
-    // lowest index bits bounds them from below (ties at the value only
-    // loosen the bound).  The smallest of the NW bounds has L distinct keys
-    // at or above it; otherwise t0 = 0 (fewer than NT keys)
-    uint64_t t0 = 0;
-    if (n >= NT) {
-        const int q = (L + NW - 1) / NW;
-        const uint32_t tv = (uint32_t)(tmax >> 32);
-        uint32_t res = 0;
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t cand_bits = res | (1u << bit);
-            if (__popcll(__ballot(tv >= cand_bits)) >= q)
-                res = cand_bits;
-        }
+        // max and log-sum-exp over the row
+        float m = x[0];
+#pragma unroll
+        for (int i = 1; i < NV; ++i)
+            m = __builtin_fmaxf(m, x[i]);
+        m = wave_allreduce(m, [](float a, float c) { return __builtin_fmaxf(a, c); });
         if (lane == 0)
-            tq[wv] = (uint64_t)res << 32;
+            red[wv] = m;
         __syncthreads();
-        t0 = tq[0];
+        m = red[0];
 #pragma unroll
         for (int w = 1; w < NW; ++w)
-            t0 = tq[w] < t0 ? tq[w] : t0;
-    }
-    // the keys >= t0, compacted in thread order
-    int c = 0;
+            m = __builtin_fmaxf(m, red[w]);
+        __syncthreads();
+        float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
-        c += (tid + NT * i < n && make_key(o[i], flat0 + NT * i) >= t0) ? 1 : 0;
-    int M;
-    const int incl = block_incl_scan<NT>(c, wsum, M);
-    if (M <= SEL_CAND) {
-        int at = incl - c;
+        for (int i = 0; i < NV; ++i)
+            s += __expf(x[i] - m);
+        s = wave_allreduce(s, [](float a, float c) { return a + c; });
+        if (lane == 0)
+            red[wv] = s;
+        __syncthreads();
+        s = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            s += red[w];
+        const float off_w = p.score_old[r] - (m + __logf(s));
+        if (tid == 0)
+            p.ws_off[r] = off_w;
+
+        // the candidates' ordered value bits replace the logits; invalid
+        // slots hold 0, below every bound used with them
+        uint32_t o[NV];
+        uint32_t omax = 0;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            o[i] = valid(i) ? ord_f32(off_w + x[i]) : 0u;
+            omax = o[i] > omax ? o[i] : omax;
+        }
+        // t0: when every thread holds keys (n >= NT), each wave's q-th best
+        // thread maximum value (q = ceil(L / NW)), found bit by bit with
+        // ballots over the 32 value bits: at least q distinct keys of the
+        // wave have that value or more, so the key with that value and zero
+        // index bits bounds them from below (ties at the value only loosen
+        // the bound).  The smallest of the NW bounds has L distinct keys at
+        // or above it; otherwise t0 = 0 (fewer than NT keys)
+        uint32_t th = 0;                          // t0 = th << 32
+        if (n >= NT) {
+            const int q = (L + NW - 1) / NW;
+            uint32_t res = 0;
+            for (int bit = 31; bit >= 0; --bit) {
+                const uint32_t cand_bits = res | (1u << bit);
+                if (__popcll(__ballot(omax >= cand_bits)) >= q)
+                    res = cand_bits;
+            }
+            if (lane == 0)
+                tq[wv] = res;
+            __syncthreads();
+            th = (uint32_t)tq[0];
+#pragma unroll
+            for (int w = 1; w < NW; ++w)
+                th = (uint32_t)tq[w] < th ? (uint32_t)tq[w] : th;
+        }
+        // the keys >= t0, compacted in thread order
+        auto above = [&](int i) { return valid(i) && o[i] >= th; };
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            c += above(i) ? 1 : 0;
+        int M;
+        const int incl = block_incl_scan<NT>(c, wsum, M);
+        if (M <= SEL_CAND) {
+            int at = incl - c;
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                if (above(i))
+                    cand[at++] = make_key(o[i], flat0 + NT * i);
+            __syncthreads();
+            // rank among the candidates: the L best land in the row's list in order
+            if (tid < M) {
+                const uint64_t mine = cand[tid];
+                int rk = 0;
+                for (int j = 0; j < M; ++j)
+                    rk += cand[j] > mine ? 1 : 0;
+                if (rk < L)
+                    list[rk] = mine;
+            }
+            if (tid >= M && tid < L)              // fewer candidates than L: pad
+                list[tid] = 0;
+            return;
+        }
+        // many keys at or above t0: radix select of the L best among them
+        const uint64_t t0 = (uint64_t)th << 32;
+        hist3[tid] = 0;                           // NT == 256 bins
+        uint64_t best = 0, unused = ~0ull;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const uint64_t key = make_key(o[i], flat0 + NT * i);
-            if (tid + NT * i < n && key >= t0)
-                cand[at++] = key;
+            if (above(i) && key > best)
+                best = key;
+        }
+        block_minmax<NT>(best, unused, red64);    // its barrier publishes hist3
+        int hb = 0;
+        uint64_t pf, mk;
+        radix_kth<NT>(
+            L, best, t0,
+            [&](auto f) {
+#pragma unroll
+                for (int i = 0; i < NV; ++i)
+                    if (above(i))
+                        f(make_key(o[i], flat0 + NT * i));
+            },
+            hist3, hb, pf, mk);
+        if (tid == 0)
+            n_buf = 0;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const uint64_t key = make_key(o[i], flat0 + NT * i);
+            const bool take = above(i) && (key & mk) >= pf;
+            const int at = wave_append(take, &n_buf);
+            if (take && at < L)
+                buf[at] = key;
         }
         __syncthreads();
-        // rank among the candidates: the L best land in the row's list in order
-        if (tid < M) {
-            const uint64_t mine = cand[tid];
+        if (tid < L) {
+            const uint64_t mine = buf[tid];
             int rk = 0;
-            for (int j = 0; j < M; ++j)
-                rk += cand[j] > mine ? 1 : 0;
-            if (rk < L)
-                list[rk] = mine;
+            for (int j = 0; j < L; ++j)
+                rk += buf[j] > mine ? 1 : 0;
+            list[rk] = mine;
         }
-        if (tid >= M && tid < L)                  // fewer candidates than L: pad
-            list[tid] = 0;
-        return;
-    }
-    // many keys at or above t0: radix select of the L best among them
-    hist3[tid] = 0;                               // NT == 256 bins
-    uint64_t best = tmax, unused = ~0ull;
-    block_minmax<NT>(best, unused, red64);        // its barrier publishes hist3
-    int hb = 0;
-    uint64_t pf, mk;
-    radix_kth<NT>(
-        L, best, t0,
-        [&](auto f) {
-#pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const uint64_t key = make_key(o[i], flat0 + NT * i);
-                if (tid + NT * i < n && key >= t0)
-                    f(key);
-            }
-        },
-        hist3, hb, pf, mk);
-    if (tid == 0)
-        n_buf = 0;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const uint64_t key = make_key(o[i], flat0 + NT * i);
-        const bool take = tid + NT * i < n && key >= t0 && (key & mk) >= pf;
-        const int at = wave_append(take, &n_buf);
-        if (take && at < L)
-            buf[at] = key;
-    }
-    __syncthreads();
-    if (tid < L) {
-        const uint64_t mine = buf[tid];
-        int rk = 0;
-        for (int j = 0; j < L; ++j)
-            rk += buf[j] > mine ? 1 : 0;
-        list[rk] = mine;
-    }
+    };
+    if (n == NV * NT)                             // uniform for the workgroup
+        run(std::true_type{});
+    else
+        run(std::false_type{});
 }
 
 __device__ __forceinline__ float wave_max(float v)
