@@ -40,10 +40,13 @@ constexpr int SEL_REQ_NV = SEL_MAX_V / SEL_REQ_THREADS;   // logits per thread, 
 constexpr int SEL_CAND = SEL_ROW_THREADS;                 // keys >= the row bound kept in LDS
 constexpr int SEL_WCAND = 256;                            // the same, one wave per row
 
+// Order-preserving bits of a float: negative values complemented, the sign
+// bit set on the others (the sign, spread by an arithmetic shift, picks the
+// mask: three vector instructions)
 __device__ __forceinline__ uint32_t ord_f32(float f)
 {
     const uint32_t u = __float_as_uint(f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 __device__ __forceinline__ float unord_f32(uint32_t o)
@@ -478,10 +481,14 @@ __attribute__((amdgpu_waves_per_eu(NV <= 32 ? 5 : 2))) void select_rows(const Se
         for (int w = 1; w < NW; ++w)
             m = __builtin_fmaxf(m, red[w]);
         __syncthreads();
+        // exp(x - m) as 2^(x log2 e - m log2 e): one fused multiply-add and
+        // one v_exp_f32 per logit
+        constexpr float L2E = 1.4426950408889634f;
+        const float nm = -m * L2E;
         float s = 0.f;
 #pragma unroll
         for (int i = 0; i < NV; ++i)
-            s += __expf(x[i] - m);
+            s += __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], L2E, nm));
         s = wave_allreduce(s, [](float a, float c) { return a + c; });
         if (lane == 0)
             red[wv] = s;
@@ -673,10 +680,12 @@ __global__ __launch_bounds__(256) void select_rows_wave(const SelParams p)
     for (int i = 1; i < NL; ++i)
         m = __builtin_fmaxf(m, x[i]);
     m = wave_max(m);
+    constexpr float L2E = 1.4426950408889634f;   // exp(x - m) = 2^(x log2 e - m log2 e)
+    const float nm = -m * L2E;
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < NL; ++i)
-        s += __expf(x[i] - m);
+        s += __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], L2E, nm));
     s = wave_sum(s);
     const float off_w = score - (m + __logf(s));
     if (lane == 0)
