@@ -33,6 +33,7 @@ namespace gr {
 constexpr int SEL_ROW_THREADS = 256;
 constexpr int SEL_REQ_THREADS = 1024;
 constexpr int SEL_HEAD = 8;                               // keys per row behind the bound
+constexpr int SEL_HEAD_FAR = 6;                           // the same, rows beyond one chunk
 constexpr int SEL_HEAD_REG = 8;                           // head keys per thread in registers
 constexpr int SEL_SURV_REG = 4;                           // survivors per thread in registers
 constexpr int SEL_SURV_LDS = SEL_SURV_REG * SEL_REQ_THREADS;
@@ -846,7 +847,14 @@ __global__ __launch_bounds__(SEL_REQ_THREADS) void select_request(const SelParam
     int k_row = K < p.V ? K : p.V;
     k_row = k_row < p.K_max ? k_row : p.K_max;
     const int L = k_row < SEL_LIST ? k_row : SEL_LIST;
-    const int head = L < SEL_HEAD ? L : SEL_HEAD;
+    // Head keys per row behind the bound: all SEL_HEAD when the rows' lists
+    // fit one chunk (their heads are then read from registers), else 6 (the
+    // heads are loaded and each costs an LDS atomic in the bound's first
+    // pass; fewer of them loosen the bound a little).  Measured: 4 x 900
+    // beams 58.0 -> 55.5 us with 6 (60.7 with 4: too many survivors), 8 x
+    // 128 beams 27.2 with 8 against 27.6 with 6.
+    const int head_cap = W <= CHUNK ? SEL_HEAD : SEL_HEAD_FAR;
+    const int head = L < head_cap ? L : head_cap;
     const int K_eff = K < p.K_max ? K : p.K_max;      // keys that can be produced
     const uint64_t *lists = p.ws_list + (int64_t)r0 * SEL_LIST;
     uint64_t *surv = p.ws_surv + (int64_t)r0 * p.K_max;
