@@ -38,7 +38,12 @@ constexpr int SEL_HEAD_REG = 8;                           // head keys per threa
 constexpr int SEL_SURV_REG = 4;                           // survivors per thread in registers
 constexpr int SEL_SURV_LDS = SEL_SURV_REG * SEL_REQ_THREADS;
 constexpr int SEL_REQ_NV = SEL_MAX_V / SEL_REQ_THREADS;   // logits per thread, re-selection
-constexpr int SEL_CAND = SEL_ROW_THREADS;                 // keys >= the row bound kept in LDS
+// 512 threads of 16 candidates per row for vocabularies up to 8192 (each
+// row's chain is half as long) measured slower than 256 of 32: 8 x 128
+// beams 27.1 -> 28.2 us, 4 x 900 55.1 -> 60.3 us; kept for other builds.
+#ifndef ROW512
+#define ROW512 0
+#endif
 constexpr int SEL_WCAND = 256;                            // the same, one wave per row
 
 // Order-preserving bits of a float: negative values complemented, the sign
@@ -406,19 +411,21 @@ __device__ __forceinline__ void row_candidates(const SelParams &p, int r, bool t
     }
 }
 
-// One beam row per workgroup; NV candidates per thread (n <= NV * 256).
-// With NV <= 32 the kernel fits 96 registers, i.e. five waves per SIMD: a
-// row's loads are a third of its time, so more resident rows keep HBM busy
-// (measured: four waves 79.1 us, five 75.2 us per 4 x 900 x 8192 call).
-template <int NV, bool TRIE>
-__global__ __launch_bounds__(SEL_ROW_THREADS)
-__attribute__((amdgpu_waves_per_eu(NV <= 32 ? 5 : 2))) void select_rows(const SelParams p)
+// One beam row per workgroup of NT threads; NV candidates per thread (n <=
+// NV * NT).  With NV <= 32 the kernel fits 96 registers, i.e. five waves per
+// SIMD: a row's loads are a third of its time, so more resident rows keep
+// HBM busy (measured: four waves 79.1 us, five 75.2 us per 4 x 900 x 8192
+// call); with NV <= 16, 64 registers (eight waves).
+template <int NV, int NT, bool TRIE>
+__global__ __launch_bounds__(NT)
+__attribute__((amdgpu_waves_per_eu(NV <= 16 ? 8 : (NV <= 32 ? 5 : 2)))) void select_rows(const SelParams p)
 {
-    constexpr int NT = SEL_ROW_THREADS, NW = NT / 64;
+    constexpr int NW = NT / 64;
+    static_assert(NT % 64 == 0 && NT >= 256, "whole waves; the histograms need 256 threads");
     __shared__ float red[NW];
     __shared__ int wsum[NW];
     __shared__ uint64_t tq[NW];
-    __shared__ uint64_t cand[SEL_CAND];
+    __shared__ uint64_t cand[NT];
     __shared__ uint64_t red64[2 * NW];
     // used only when many keys tie around the bound
     __shared__ uint32_t hist3[3 * 256];
@@ -543,7 +550,7 @@ __attribute__((amdgpu_waves_per_eu(NV <= 32 ? 5 : 2))) void select_rows(const Se
             c += above(i) ? 1 : 0;
         int M;
         const int incl = block_incl_scan<NT>(c, wsum, M);
-        if (M <= SEL_CAND) {
+        if (M <= NT) {
             int at = incl - c;
 #pragma unroll
             for (int i = 0; i < NV; ++i)
@@ -565,7 +572,8 @@ __attribute__((amdgpu_waves_per_eu(NV <= 32 ? 5 : 2))) void select_rows(const Se
         }
         // many keys at or above t0: radix select of the L best among them
         const uint64_t t0 = (uint64_t)th << 32;
-        hist3[tid] = 0;                           // NT == 256 bins
+        if (tid < 256)
+            hist3[tid] = 0;
         uint64_t best = 0, unused = ~0ull;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
@@ -1173,24 +1181,28 @@ hipError_t launch_beam_select(const SelParams &p, hipStream_t s)
         // the dependent loads dominates), else one workgroup per row (long
         // rows: a wave holding 64 * 32 or more keys runs at low occupancy)
         const int n = p.node_ptr ? p.max_fanout : p.V;
-        const dim3 gw((p.R_old + 3) / 4), g(p.R_old), t(SEL_ROW_THREADS);
+        const dim3 gw((p.R_old + 3) / 4), g(p.R_old), t(SEL_ROW_THREADS), t2(2 * SEL_ROW_THREADS);
         if (p.node_ptr) {
             if (n <= 64 * 4)
                 hipLaunchKernelGGL((select_rows_wave<4, true>), gw, t, 0, s, p);
             else if (n <= 64 * 16)
                 hipLaunchKernelGGL((select_rows_wave<16, true>), gw, t, 0, s, p);
+            else if (ROW512 && n <= 16 * 2 * SEL_ROW_THREADS)
+                hipLaunchKernelGGL((select_rows<16, 2 * SEL_ROW_THREADS, true>), g, t2, 0, s, p);
             else if (n <= 32 * SEL_ROW_THREADS)
-                hipLaunchKernelGGL((select_rows<32, true>), g, t, 0, s, p);
+                hipLaunchKernelGGL((select_rows<32, SEL_ROW_THREADS, true>), g, t, 0, s, p);
             else
-                hipLaunchKernelGGL((select_rows<64, true>), g, t, 0, s, p);
+                hipLaunchKernelGGL((select_rows<32, 2 * SEL_ROW_THREADS, true>), g, t2, 0, s, p);
         } else if (n <= 64 * 4) {
             hipLaunchKernelGGL((select_rows_wave<4, false>), gw, t, 0, s, p);
         } else if (n <= 64 * 16) {
             hipLaunchKernelGGL((select_rows_wave<16, false>), gw, t, 0, s, p);
+        } else if (ROW512 && n <= 16 * 2 * SEL_ROW_THREADS) {
+            hipLaunchKernelGGL((select_rows<16, 2 * SEL_ROW_THREADS, false>), g, t2, 0, s, p);
         } else if (n <= 32 * SEL_ROW_THREADS) {
-            hipLaunchKernelGGL((select_rows<32, false>), g, t, 0, s, p);
+            hipLaunchKernelGGL((select_rows<32, SEL_ROW_THREADS, false>), g, t, 0, s, p);
         } else {
-            hipLaunchKernelGGL((select_rows<64, false>), g, t, 0, s, p);
+            hipLaunchKernelGGL((select_rows<32, 2 * SEL_ROW_THREADS, false>), g, t2, 0, s, p);
         }
     }
     if (p.B > 0)
