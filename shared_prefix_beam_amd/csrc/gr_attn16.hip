@@ -181,10 +181,24 @@ void fused_decode_attn16(const Params p)
     const uint16_t *kv_v = p.ctx_v + ((PAGED ? 0 : (int64_t)b * p.ctx_cap * p.Hkv) + g) * D;
     const int kv_tok = p.Hkv * D;
     const int32_t *ptab = PAGED ? p.page_table + (int64_t)b * p.pages_per_req : nullptr;
-    auto page_row = [&](int tok) -> int64_t {
-        int pg = ((const __attribute__((address_space(4))) int32_t *)(uintptr_t)ptab)[tok / p.page_size];
-        pg = pg < 0 ? 0 : (pg >= p.n_pages ? (int)(p.n_pages - 1) : pg);
-        return ((int64_t)pg * p.page_size + tok % p.page_size) * kv_tok;
+    // Page arithmetic without integer division when the page size is a
+    // power of two (a runtime divide costs dozens of scalar instructions,
+    // and every tile needs two).
+    const int ps = PAGED ? p.page_size : 1;
+    const bool ps_pow2 = (ps & (ps - 1)) == 0;
+    const int ps_shift = __builtin_ctz((unsigned)ps);
+    auto page_idx = [&](int tok) { return ps_pow2 ? tok >> ps_shift : tok / ps; };
+    auto page_off = [&](int tok) { return ps_pow2 ? (tok & (ps - 1)) : tok % ps; };
+    // An entry outside the pool is clamped into it (the pool size fits 32
+    // bits): a broken table reads wrong data, never outside the buffer.
+    const int pg_last = PAGED ? (int)(p.n_pages - 1) : 0;
+    auto page_clamp = [&](int pg) { return pg < 0 ? 0 : (pg > pg_last ? pg_last : pg); };
+    auto page_entry = [&](int tok) -> int {    // wave-uniform table read
+        return ((const __attribute__((address_space(4))) int32_t *)(uintptr_t)ptab)[page_idx(tok)];
+    };
+    // element offset of row `tok - sub` in the pool, `tok` lying in page `pg`
+    auto page_base = [&](int pg, int tok, int sub) -> int64_t {
+        return ((int64_t)page_clamp(pg) * ps + page_off(tok) - sub) * kv_tok;
     };
     constexpr int RPL = 1024 / Gm::ROW;
     constexpr int LPW = (Gm::LOADS + NQT - 1) / NQT;
@@ -204,15 +218,19 @@ void fused_decode_attn16(const Params p)
         const uint32_t dst0 = lds0 + stream_off + buf * Gm::TILE;
         if constexpr (PAGED) {
             if (key0 + KT <= L) {
+                // the tile's first and last 16 keys each lie in one page
+                // (page sizes are multiples of 16, tiles start at multiples
+                // of 32): one base per half, the lane offsets the dense ones
+                const int64_t base0 = page_base(page_entry(key0), key0, 0);
+                const int64_t base1 = page_base(page_entry(key0 + 16), key0 + 16, 16);
 #pragma unroll
                 for (int i = 0; i < LPW; ++i) {
                     const int u = qt + i * NQT;
                     if (EVEN || u < Gm::LOADS) {
                         const bool is_v = u >= Gm::LOADS / 2;
                         const int uu = is_v ? u - Gm::LOADS / 2 : u;
-                        const int tok0 = key0 + uu * RPL;
-                        dma16_s((is_v ? kv_v : kv_k) + page_row(tok0) - (int64_t)uu * RPL * kv_tok,
-                                loff[i], dst0 + (is_v ? Gm::KBYTES : 0) + uu * 1024);
+                        dma16_s((is_v ? kv_v : kv_k) + (uu * RPL < 16 ? base0 : base1), loff[i],
+                                dst0 + (is_v ? Gm::KBYTES : 0) + uu * 1024);
                     }
                 }
             } else {
@@ -226,9 +244,7 @@ void fused_decode_attn16(const Params p)
                     const int r = uu * RPL + lane / Gm::CH;
                     const int c = (lane % Gm::CH) ^ (is_v ? vswz16<D>(r) : kswz16<D>(r));
                     const int tok = key0 + r < L ? key0 + r : L - 1;
-                    int pg = ptab[tok / p.page_size];
-                    pg = pg < 0 ? 0 : (pg >= p.n_pages ? (int)(p.n_pages - 1) : pg);
-                    const int64_t row = ((int64_t)pg * p.page_size + tok % p.page_size) * kv_tok;
+                    const int64_t row = page_base(ptab[page_idx(tok)], tok, 0);
                     dma16((is_v ? kv_v : kv_k) + row + 8 * c,
                           dst0 + (is_v ? Gm::KBYTES : 0) + uu * 1024);
                 }

@@ -35,7 +35,7 @@ def ragged(D=128, Hq=16, Hkv=8, seed=0):
                     beam_len=[3, 1, 5], seed=seed)
 
 
-@pytest.mark.parametrize("page_size", [16, 32, 64, 128])
+@pytest.mark.parametrize("page_size", [16, 32, 48, 64, 80, 128])
 def test_paged_ragged_all_rows(page_size):
     inp = ragged(seed=page_size)
     pg = I.to_paged(inp, page_size, seed=page_size + 1)
@@ -83,6 +83,22 @@ def test_paged_every_tiling(tiling, split):
 
 TILINGS16 = [(128, 4, 2), (128, 8, 1), (128, 4, 1), (128, 6, 1), (128, 2, 2), (64, 4, 2),
              (64, 8, 1)]
+
+
+@pytest.mark.parametrize("page_size", [16, 48], ids=["p16", "p48"])
+@pytest.mark.parametrize("tiling", [(4, 2, 1, True), (4, 1, 1, False)], ids=["row16_q4_k2", "q4_k1"])
+def test_paged_long_context(tiling, page_size):
+    """A 17k-token context over more than a thousand pages, with a page size
+    that is a power of two (shift and mask) and one that is not (division):
+    bitwise equal to the dense launch."""
+    inp = I.custom(B=2, Hq=16, Hkv=8, D=128, W=[9, 40], ctx_len=[16993, 700],
+                   beam_len=[2, 3], seed=77)
+    pg = I.to_paged(inp, page_size, seed=78)
+    assert pg.page_table.shape[1] * page_size >= 16993
+    log(f"[paged] long context, {pg.page_table.shape[1]} pages of {page_size}, tiling {tiling}")
+    out, lse = run_paged(inp, pg, tiling=tiling)
+    dense_out, dense_lse = run_lib(inp, "fused", tiling=tiling)
+    assert np.array_equal(out, dense_out) and np.array_equal(lse, dense_lse)
 
 
 @pytest.mark.parametrize("tiling", TILINGS16, ids=[f"d{d}_q{a}_k{c}" for d, a, c in TILINGS16])
