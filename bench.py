@@ -957,8 +957,11 @@ def main():
         t = r["launch_ms"] * 1e-3
         paged.append({"workload": r["inp"].wl.name, "page_size": PAGE_SIZE,
                       "launch_us": r["launch_ms"] * 1e3,
+                      "launch_us_median": r["launch_median_ms"] * 1e3,
+                      "launch_us_min": r["launch_min_ms"] * 1e3,
                       "hbm_GBps": r["nbytes"] / t / 1e9, "TFLOPs": r["flops"] / t / 1e12,
                       "vs_dense_launch": dense["launch_ms"] / r["launch_ms"],
+                      "vs_dense_launch_median": dense["launch_median_ms"] / r["launch_median_ms"],
                       "spot_check": {"max_abs": r["spot_abs"], "lse_abs": r["spot_lse"]}})
     line["paged"] = paged
     line["measured_peaks"] = peaks
