@@ -90,6 +90,19 @@ def test_small_shapes_all_rows(case, which):
     assert_parity(out, lse, ref_out, ref_lse, f"{name}/{which}")
 
 
+def test_long_context_all_rows():
+    """A 131,072-token context shared by six beams, beside a short request:
+    the planner splits each pair's context over eight workgroups of 512
+    tiles each.  Every row against the oracle (fused path only: the generic
+    comparator is limited to 16,384 keys)."""
+    inp = I.custom(B=2, Hq=16, Hkv=8, D=128, W=[6, 3], ctx_len=[131072, 100], beam_len=[3, 2],
+                   seed=4242)
+    log(f"[parity] long context L={inp.ctx_len.tolist()} R={inp.R}")
+    out, lse = run_lib(inp, "fused")
+    ref_out, ref_lse = O.decode_attn_inputs(inp)
+    assert_parity(out, lse, ref_out, ref_lse, "long context")
+
+
 TILINGS = [(128, 8, 1), (128, 4, 1), (128, 4, 2), (128, 2, 2), (64, 4, 1), (64, 2, 2), (64, 2, 4)]
 SPLITS = [1, 2, 3, 8]
 
