@@ -190,8 +190,9 @@ def write_profile_summaries(d: str):
     f_fetch, copy_fetch_kib = _copy_factor(os.path.join(d, "copy_fetch"), "FETCH_SIZE")
     f_write, copy_write_kib = _copy_factor(os.path.join(d, "copy_write"), "WRITE_SIZE")
     sha = kernel_hash()
-    for which, cfg in (("primary", PRIMARY), ("secondary", SECONDARY), ("cfg1", 1), ("cfg3", 3),
-                       ("cfg5", 5)):
+    for which, cfg, page in (("primary", PRIMARY, None), ("secondary", SECONDARY, None),
+                             ("cfg1", 1, None), ("cfg3", 3, None), ("cfg5", 5, None),
+                             ("paged2", 2, PAGE_SIZE), ("paged4", 4, PAGE_SIZE)):
         if not os.path.isdir(os.path.join(d, f"trace_{which}")):
             continue                                # not profiled in this folder
         wl = I.WORKLOADS[cfg]
@@ -203,9 +204,14 @@ def write_profile_summaries(d: str):
         traffic = fetch_kib * 1024 * f_fetch + write_kib * 1024 * f_write
         inp = I.generate(wl)
         nbytes, flops = algorithmic(inp)
+        tag = wl.name if page is None else f"paged{page}_{wl.name}"
+        title = wl.name if page is None else f"{wl.name}, ContextKV in pages of {page} tokens"
+        if page is not None:
+            # plus each request's page table, read once
+            nbytes += 4 * inp.B * max(-(-inp.ctx_cap // page), 1)
         kern = [r for r in stats if "fused_decode_attn" in r["Name"]]
         kname = kern[0]["Name"] if kern else "fused_decode_attn"
-        lines = [f"# fused decode attention on {wl.name}", "", f"kernel: {kname}", "",
+        lines = [f"# fused decode attention on {title}", "", f"kernel: {kname}", "",
                  "kernel trace (rocprofv3 --kernel-trace --stats), command from the repository root:",
                  "    " + PROFILE_COMMANDS["trace"].format(d="gpurun_out/prof", w=which), "",
                  f"{'kernel':60s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
@@ -232,9 +238,9 @@ def write_profile_summaries(d: str):
                   f"average launch            {avg_us:12.2f} us -> "
                   f"{nbytes / avg_us / 1e3:.1f} GB/s, {flops / avg_us / 1e6:.1f} TFLOP/s",
                   f"kernel sources sha256[:16] {sha}"]
-        name = f"fused_decode_attn_{wl.name}"
+        name = f"fused_decode_attn_{tag}"
         open(os.path.join(out_dir, name + ".txt"), "w").write("\n".join(lines) + "\n")
-        json.dump({"kernel": kname, "workload": wl.name, "kernel_sha": sha,
+        json.dump({"kernel": kname, "workload": tag, "kernel_sha": sha,
                    "bytes_per_launch": traffic, "fetch_kib": fetch_kib, "write_kib": write_kib,
                    "fetch_factor": f_fetch, "write_factor": f_write, "avg_launch_us": avg_us},
                   open(os.path.join(out_dir, f"traffic_{name}.json"), "w"), indent=1)
@@ -828,7 +834,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", choices=["primary", "secondary", "cfg1", "cfg2", "cfg3", "cfg4",
-                                       "cfg5", "beam_step", "select", "trie"],
+                                       "cfg5", "paged2", "paged4", "beam_step", "select", "trie"],
                     help="time one workload only and print its launch time (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run 10 device copies of 256 MiB (reference for HBM byte counters)")
@@ -874,10 +880,11 @@ def main():
                           "bit_exact": r["bit_exact"]}), flush=True)
         return
     if args.only:
+        paged = args.only.startswith("paged")
         cfg = {"primary": PRIMARY, "secondary": SECONDARY}.get(args.only)
-        cfg = cfg if cfg is not None else int(args.only[3:])
-        r = measure(cfg, args.steps, args.warmup, reps=1, latency_calls=0,
-                    settle=lambda: measured_peaks(reps=2))
+        cfg = cfg if cfg is not None else int(args.only[5:] if paged else args.only[3:])
+        r = measure(cfg, args.steps, args.warmup, page_size=PAGE_SIZE if paged else None, reps=1,
+                    latency_calls=0, settle=lambda: measured_peaks(reps=2))
         print(json.dumps({"workload": r["inp"].wl.name, "launch_us": r["launch_ms"] * 1e3,
                           "ms_per_step": r["ms_per_step"]}), flush=True)
         return
@@ -962,6 +969,7 @@ def main():
                       "hbm_GBps": r["nbytes"] / t / 1e9, "TFLOPs": r["flops"] / t / 1e12,
                       "vs_dense_launch": dense["launch_ms"] / r["launch_ms"],
                       "vs_dense_launch_median": dense["launch_median_ms"] / r["launch_median_ms"],
+                      "traffic": recorded_traffic(f"paged{PAGE_SIZE}_{r['inp'].wl.name}"),
                       "spot_check": {"max_abs": r["spot_abs"], "lse_abs": r["spot_lse"]}})
     line["paged"] = paged
     line["measured_peaks"] = peaks
