@@ -63,3 +63,51 @@ def test_noalloc_matches_workspace_entry_point(order):
         assert np.array_equal(out, ref_out) and np.array_equal(lse, ref_lse), name
         o_out, o_lse = O.decode_attn_inputs(inp)
         assert_parity(out, lse, o_out, o_lse, f"noalloc {name}")
+
+
+def test_noalloc_random_shapes_in_a_row():
+    """The seeded random shapes of test_gpu_random.py, one after another
+    through both entry points (the scratch keeps each call's leftovers):
+    bitwise equal where the split fits the library's scratch, refused with
+    GR_ERR_WORKSPACE exactly where it does not (counters beyond 64 KB or
+    partials beyond the rest of the 16 MB)."""
+    import torch
+    from shared_prefix_beam_amd import gr_attn
+    from test_gpu_random import N_CASES, draw
+    scratch, counters = 16 << 20, 64 << 10
+    n_run = 0
+    for seed in range(N_CASES):
+        D, Hq, Hkv, B, W, L, T, kw = draw(seed)
+        inp = I.custom(B=B, Hq=Hq, Hkv=Hkv, D=D, W=W, ctx_len=L, beam_len=T, seed=seed, **kw)
+        t = I.to_torch(inp)
+        W_max = int(max(inp.wl.W))
+        dims = gr_attn.make_dims(t["q"], t["ctx_k"], t["beam_k"], t["beam_path"], W_max)
+        need = int(gr_attn.gr_decode_attn_workspace_bytes(dims))
+        pl = gr_attn.plan(dims)
+        refuse = False
+        if need > 0:
+            pairs = inp.B * Hkv
+            n_qt = pl["grid"] // (8 * (-(-pairs // 8)) * pl["n_split"])
+            count_bytes = pairs * n_qt * 4
+            part = need - (-(-count_bytes // 256)) * 256
+            refuse = count_bytes > counters or part > scratch - counters
+        log(f"[noalloc random {seed}] plan={pl} workspace={need} refused={refuse}")
+        out = torch.full_like(t["q"], float("nan"))
+        lse = torch.full(t["q"].shape[:2], float("nan"), dtype=torch.float32, device="cuda")
+        st = gr_attn.gr_decode_attn_noalloc(
+            dims, t["row_offset"].data_ptr(), t["q"].data_ptr(), t["ctx_k"].data_ptr(),
+            t["ctx_v"].data_ptr(), t["ctx_len"].data_ptr(), t["beam_k"].data_ptr(),
+            t["beam_v"].data_ptr(), t["beam_path"].data_ptr(), t["beam_len"].data_ptr(),
+            out.data_ptr(), lse.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        if refuse:
+            assert st == gr_attn.GR_ERR_WORKSPACE, (seed, gr_attn.gr_status_str(st))
+            continue
+        assert st == gr_attn.GR_OK, (seed, gr_attn.gr_status_str(st))
+        torch.cuda.synchronize()
+        ref_out, ref_lse = gr_attn.decode_attn(t["q"], t["ctx_k"], t["ctx_v"], t["ctx_len"],
+                                               t["beam_k"], t["beam_v"], t["beam_path"],
+                                               t["beam_len"], t["row_offset"], W_max=W_max)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), seed
+        n_run += 1
+    assert n_run > 0
