@@ -488,10 +488,13 @@ void fused_decode_attn16(const Params p)
                     sync_tile(it + 1, it);
                 else
                     block_barrier();
-                if (it + NBUF - 1 < n_mine)
-                    issue_tile(it + NBUF - 1, (it + NBUF - 1) % NBUF);
+                // the V reads go first into the LDS queue, then this wave's
+                // share of the refill (measured ~1% faster than the refill
+                // first), then the K reads
                 bf16x8 vf[G16::DB];
                 vread(it % NBUF, vf);
+                if (it + NBUF - 1 < n_mine)
+                    issue_tile(it + NBUF - 1, (it + NBUF - 1) % NBUF);
                 u32x4 kf[2][G16::DC];
                 if constexpr (HAS_NEXT)
                     kread((it + 1) % NBUF, kf);
