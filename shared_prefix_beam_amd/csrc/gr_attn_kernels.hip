@@ -425,7 +425,10 @@ void fused_decode_attn(const Params p)
             auto one = [&](auto buf_tag) {
                 if (it < n_mine) {
                     step(it);
-                    compute_tile(it, buf_tag, first_max && it == 0, accum_tag);
+                    // a max-only pass takes every tile's maximum; an
+                    // accumulating one fixes its reference at the first tile
+                    compute_tile(it, buf_tag, !decltype(accum_tag)::value || (first_max && it == 0),
+                                 accum_tag);
                     ++it;
                 }
             };

@@ -125,3 +125,28 @@ def test_paged_workloads(cfg, page_size):
                                            ctx_cap=inp.ctx_cap, scale=inp.scale)
     assert np.isfinite(out).all()
     assert_parity(out, lse, ref_out, ref_lse, f"paged cfg{cfg}")
+
+
+@pytest.mark.parametrize("page_size", [16, 48], ids=["p16", "p48"])
+@pytest.mark.parametrize("tiling", [(4, 1, 1, False), (4, 1, 3, False), (4, 2, 1, True)],
+                         ids=["q4_k1", "q4_k1_s3", "row16_q4_k2"])
+def test_paged_rising_scores_take_exact_sweep(tiling, page_size):
+    """Scores that grow by far more than 44 nats along the context: the exact
+    re-sweep runs, and reads the pages a second time through the table."""
+    inp = I.custom(B=2, Hq=16, Hkv=8, D=128, W=[40, 7], ctx_len=[600, 250], beam_len=[2, 3],
+                   seed=9)
+    k = I.bf16_bits_to_f32(inp.ctx_k).copy()
+    ramp = np.linspace(0.05, 6.0, inp.ctx_cap, dtype=np.float32)[None, :, None, None]
+    inp.ctx_k[:] = I.to_bf16_bits(k * ramp)
+    inp.q[:] = I.to_bf16_bits(I.bf16_bits_to_f32(inp.q) * np.float32(4.0))
+    pg = I.to_paged(inp, page_size, seed=10)
+    log(f"[paged] rising scores (exact re-sweep) page {page_size} tiling {tiling}")
+    out, lse = run_paged(inp, pg, tiling=tiling)
+    ref_out, ref_lse = O.decode_attn_paged(inp.q, pg.k_pages, pg.v_pages, pg.page_table,
+                                           page_size, inp.ctx_len, inp.beam_k, inp.beam_v,
+                                           inp.beam_path, inp.beam_len, inp.row_offset,
+                                           ctx_cap=inp.ctx_cap, scale=inp.scale)
+    assert (ref_lse > 60).any()
+    assert_parity(out, lse, ref_out, ref_lse, f"paged rising {page_size} {tiling}")
+    dense_out, dense_lse = run_lib(inp, "fused", tiling=tiling)
+    assert np.array_equal(out, dense_out) and np.array_equal(lse, dense_lse)

@@ -75,6 +75,9 @@ SMALL = [
     # BeamPath tables larger than the staged 4 KB (entries loaded per lane)
     ("ptab_overflow_g1", 1, 8, 8, 128, [150], [300], [9], {}),
     ("ptab_overflow_g2", 2, 16, 8, 128, [100, 64], [200, 129], [17, 12], {}),
+    # one very wide request: 2048 beams x 8 query heads = 16384 stacked rows
+    # on a single (request, KV head) pair (128 query tiles of one pair)
+    ("wide_2048_beams_g8", 1, 8, 1, 128, [2048], [200], [3], dict(dup_frac=0.3)),
 ]
 
 
@@ -180,9 +183,11 @@ def test_split_is_deterministic():
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
-def test_rising_scores_take_exact_sweep():
-    """Scores that grow by far more than 44 nats along the context: the
-    fixed first-tile reference would overflow, so the exact sweep must run."""
+def rising_inputs():
+    """Scores that grow by far more than 44 nats along the context: a
+    workgroup whose sweep starts at the first tile overflows its fixed
+    first-tile reference, so the exact re-sweep (max pass, then accumulation)
+    must run."""
     inp = I.custom(B=1, Hq=16, Hkv=8, D=128, W=[40], ctx_len=[600], beam_len=[2], seed=9)
     k = I.bf16_bits_to_f32(inp.ctx_k).copy()
     ramp = np.linspace(0.05, 6.0, inp.ctx_cap, dtype=np.float32)[None, :, None, None]
@@ -190,11 +195,24 @@ def test_rising_scores_take_exact_sweep():
     q = I.bf16_bits_to_f32(inp.q) * np.float32(4.0)
     inp.ctx_k[:] = I.to_bf16_bits(k)
     inp.q[:] = I.to_bf16_bits(q)
-    log("[parity] rising scores (exact re-sweep)")
-    out, lse = run_lib(inp)
+    # some (row, head) has its context maximum more than 64 (log2 units)
+    # above its first tile's: the fixed-reference sums cannot hold it
+    qq = I.bf16_bits_to_f32(inp.q).astype(np.float64)
+    kk = I.bf16_bits_to_f32(inp.ctx_k)[0].astype(np.float64)
+    s = np.einsum("rhd,lhd->rhl", qq, np.repeat(kk, 2, axis=1)) * inp.scale / np.log(2.0)
+    assert (s.max(axis=2) - s[:, :, :32].max(axis=2)).max() > 64
+    return inp
+
+
+@pytest.mark.parametrize("tiling", [None, (4, 1, 1), (8, 1, 1), (4, 2, 1), (2, 2, 1), (4, 1, 2)],
+                         ids=["planner", "q4_k1", "q8_k1", "q4_k2", "q2_k2", "q4_k1_s2"])
+def test_rising_scores_take_exact_sweep(tiling):
+    inp = rising_inputs()
+    log(f"[parity] rising scores (exact re-sweep) tiling {tiling}")
+    out, lse = run_lib(inp, tiling=tiling)
     ref_out, ref_lse = O.decode_attn_inputs(inp)
     assert (ref_lse > 60).any()
-    assert_parity(out, lse, ref_out, ref_lse, "rising")
+    assert_parity(out, lse, ref_out, ref_lse, f"rising {tiling}")
 
 
 def test_beam_dominant_and_context_dominant_rows():
