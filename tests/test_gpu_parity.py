@@ -183,24 +183,27 @@ def test_split_is_deterministic():
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
-def rising_inputs():
+def rising_inputs(D=128, Hq=16, Hkv=8, W=(40,), ctx_len=(600,), beam_len=(2,), q_mult=4.0):
     """Scores that grow by far more than 44 nats along the context: a
     workgroup whose sweep starts at the first tile overflows its fixed
     first-tile reference, so the exact re-sweep (max pass, then accumulation)
     must run."""
-    inp = I.custom(B=1, Hq=16, Hkv=8, D=128, W=[40], ctx_len=[600], beam_len=[2], seed=9)
+    inp = I.custom(B=len(W), Hq=Hq, Hkv=Hkv, D=D, W=list(W), ctx_len=list(ctx_len),
+                   beam_len=list(beam_len), seed=9)
     k = I.bf16_bits_to_f32(inp.ctx_k).copy()
     ramp = np.linspace(0.05, 6.0, inp.ctx_cap, dtype=np.float32)[None, :, None, None]
     k = k * ramp
-    q = I.bf16_bits_to_f32(inp.q) * np.float32(4.0)
+    q = I.bf16_bits_to_f32(inp.q) * np.float32(q_mult)
     inp.ctx_k[:] = I.to_bf16_bits(k)
     inp.q[:] = I.to_bf16_bits(q)
-    # some (row, head) has its context maximum more than 64 (log2 units)
-    # above its first tile's: the fixed-reference sums cannot hold it
-    qq = I.bf16_bits_to_f32(inp.q).astype(np.float64)
-    kk = I.bf16_bits_to_f32(inp.ctx_k)[0].astype(np.float64)
-    s = np.einsum("rhd,lhd->rhl", qq, np.repeat(kk, 2, axis=1)) * inp.scale / np.log(2.0)
-    assert (s.max(axis=2) - s[:, :, :32].max(axis=2)).max() > 64
+    # some (row, head) of request 0 has its context maximum more than 64
+    # (log2 units) above its first tile's: fixed-reference sums cannot hold it
+    G = Hq // Hkv
+    n0 = int(inp.row_offset[1])
+    qq = I.bf16_bits_to_f32(inp.q)[:n0].astype(np.float64)
+    kk = I.bf16_bits_to_f32(inp.ctx_k)[0, :int(inp.ctx_len[0])].astype(np.float64)
+    sc = np.einsum("rhd,lhd->rhl", qq, np.repeat(kk, G, axis=1)) * inp.scale / np.log(2.0)
+    assert (sc.max(axis=2) - sc[:, :, :32].max(axis=2)).max() > 64
     return inp
 
 
@@ -213,6 +216,44 @@ def test_rising_scores_take_exact_sweep(tiling):
     ref_out, ref_lse = O.decode_attn_inputs(inp)
     assert (ref_lse > 60).any()
     assert_parity(out, lse, ref_out, ref_lse, f"rising {tiling}")
+
+
+RISING_MORE = [
+    # (name, D, Hq, Hkv, tiling)
+    ("d64_q4_k1", 64, 8, 4, (4, 1, 1)),
+    ("d64_q2_k2", 64, 8, 4, (2, 2, 1)),
+    ("d64_q2_k4", 64, 8, 4, (2, 4, 1)),
+    ("d64_planner", 64, 8, 4, None),
+    ("g3_q4_k1", 128, 24, 8, (4, 1, 1)),
+    ("g3_planner", 128, 24, 8, None),
+    ("g8_q4_k1", 128, 8, 1, (4, 1, 1)),
+]
+
+
+@pytest.mark.parametrize("case", RISING_MORE, ids=[c[0] for c in RISING_MORE])
+def test_rising_scores_more_shapes(case):
+    """The exact re-sweep at D = 64, with per-lane BeamKV gathers (G = 3) and
+    at G = 8, on two ragged requests (the second with a short context)."""
+    name, D, Hq, Hkv, tiling = case
+    inp = rising_inputs(D=D, Hq=Hq, Hkv=Hkv, W=(40, 7), ctx_len=(600, 250), beam_len=(2, 3),
+                        q_mult=4.0 if D == 128 else 6.0)
+    log(f"[parity] rising scores {name} tiling {tiling}")
+    out, lse = run_lib(inp, tiling=tiling)
+    ref_out, ref_lse = O.decode_attn_inputs(inp)
+    assert_parity(out, lse, ref_out, ref_lse, f"rising {name}")
+
+
+@pytest.mark.parametrize("tiling", TILINGS16, ids=[f"d{d}_q{a}_k{c}" for d, a, c in TILINGS16])
+def test_row16_rising_every_tiling(tiling):
+    """The 16-row kernel's exact re-sweep (its own max-only pass) on every
+    compiled 16-row tiling, with and without beam waves."""
+    D, nqt, nks = tiling
+    inp = rising_inputs(D=D, Hq=16 if D == 128 else 8, Hkv=8 if D == 128 else 4, W=(40, 7),
+                        ctx_len=(600, 250), beam_len=(2, 3), q_mult=4.0 if D == 128 else 6.0)
+    log(f"[parity] row16 rising scores tiling {tiling}")
+    out, lse = run_lib(inp, "fused", tiling=(nqt, nks, 1, True))
+    ref_out, ref_lse = O.decode_attn_inputs(inp)
+    assert_parity(out, lse, ref_out, ref_lse, f"row16 rising {tiling}")
 
 
 def test_beam_dominant_and_context_dominant_rows():
