@@ -147,6 +147,35 @@ def test_row16_tilings_ragged(tiling, G):
     assert_parity(out, lse, ref_out, ref_lse, f"row16 {tiling} G={G}")
 
 
+@pytest.mark.parametrize("tiling", TILINGS, ids=[f"d{d}_q{a}_k{c}" for d, a, c in TILINGS])
+def test_many_steps_short_context(tiling):
+    """The 32-row kernel with more BeamKV steps than its gather area holds at
+    once (chunks of steps) against contexts of zero to two tiles."""
+    D, nqt, nks = tiling
+    Hq, Hkv = (16, 8) if D == 128 else (8, 4)
+    inp = I.custom(B=3, Hq=Hq, Hkv=Hkv, D=D, W=[37, 5, 20], ctx_len=[0, 33, 64],
+                   beam_len=[17, 9, 17], seed=400 + nqt * 10 + nks + D)
+    log(f"[parity] many steps D={D} NQT={nqt} NKS={nks} R={inp.R}")
+    out, lse = run_lib(inp, "fused", tiling=(nqt, nks, 1))
+    ref_out, ref_lse = O.decode_attn_inputs(inp)
+    assert_parity(out, lse, ref_out, ref_lse, f"many steps {tiling}")
+
+
+@pytest.mark.parametrize("tiling", TILINGS16, ids=[f"d{d}_q{a}_k{c}" for d, a, c in TILINGS16])
+def test_row16_many_steps_short_context(tiling):
+    """More BeamKV steps than the sweep has barriers (contexts of zero to two
+    tiles against 9 and 17 path tokens): beam waves fold the remaining steps
+    after the sweep's last barrier, sweep waves fold theirs before it."""
+    D, nqt, nks = tiling
+    Hq, Hkv = (16, 8) if D == 128 else (8, 4)
+    inp = I.custom(B=3, Hq=Hq, Hkv=Hkv, D=D, W=[37, 5, 20], ctx_len=[0, 33, 64],
+                   beam_len=[17, 9, 17], seed=300 + nqt * 10 + nks + D)
+    log(f"[parity] row16 many steps D={D} NQT={nqt} NKS={nks} R={inp.R}")
+    out, lse = run_lib(inp, "fused", tiling=(nqt, nks, 1, True))
+    ref_out, ref_lse = O.decode_attn_inputs(inp)
+    assert_parity(out, lse, ref_out, ref_lse, f"row16 many steps {tiling}")
+
+
 @pytest.mark.parametrize("cfg,tiling", [(2, (4, 2)), (4, (6, 1)), (4, (8, 1)), (3, (6, 1)),
                                         (5, (6, 1))])
 def test_row16_workloads(cfg, tiling):
