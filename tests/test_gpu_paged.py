@@ -69,13 +69,14 @@ def test_paged_d64(Hq, Hkv):
 TILINGS = [(128, 8, 1), (128, 4, 1), (128, 4, 2), (128, 2, 2), (64, 4, 1), (64, 2, 2), (64, 2, 4)]
 
 
+@pytest.mark.parametrize("page_size", [16, 48], ids=["p16", "p48"])
 @pytest.mark.parametrize("split", [1, 3], ids=["s1", "s3"])
 @pytest.mark.parametrize("tiling", TILINGS, ids=[f"d{d}_q{a}_k{c}" for d, a, c in TILINGS])
-def test_paged_every_tiling(tiling, split):
+def test_paged_every_tiling(tiling, split, page_size):
     D, nqt, nks = tiling
     inp = ragged(D=D, Hq=16 if D == 128 else 8, Hkv=8 if D == 128 else 4, seed=nqt * 7 + nks)
-    pg = I.to_paged(inp, 16, seed=3)
-    log(f"[paged] tiling {tiling} split {split}")
+    pg = I.to_paged(inp, page_size, seed=3)
+    log(f"[paged] tiling {tiling} split {split} page {page_size}")
     out, lse = run_paged(inp, pg, tiling=(nqt, nks, split))
     dense_out, dense_lse = run_lib(inp, "fused", tiling=(nqt, nks, split))
     assert np.array_equal(out, dense_out) and np.array_equal(lse, dense_lse)
@@ -101,13 +102,14 @@ def test_paged_long_context(tiling, page_size):
     assert np.array_equal(out, dense_out) and np.array_equal(lse, dense_lse)
 
 
+@pytest.mark.parametrize("page_size", [16, 48], ids=["p16", "p48"])
 @pytest.mark.parametrize("tiling", TILINGS16, ids=[f"d{d}_q{a}_k{c}" for d, a, c in TILINGS16])
-def test_paged_row16_tilings(tiling):
+def test_paged_row16_tilings(tiling, page_size):
     """16-row waves on a paged context: bitwise equal to the dense launch."""
     D, nqt, nks = tiling
     inp = ragged(D=D, Hq=16 if D == 128 else 8, Hkv=8 if D == 128 else 4, seed=nqt * 5 + nks)
-    pg = I.to_paged(inp, 16, seed=4)
-    log(f"[paged] row16 tiling {tiling}")
+    pg = I.to_paged(inp, page_size, seed=4)
+    log(f"[paged] row16 tiling {tiling} page {page_size}")
     out, lse = run_paged(inp, pg, tiling=(nqt, nks, 1, True))
     dense_out, dense_lse = run_lib(inp, "fused", tiling=(nqt, nks, 1, True))
     assert np.array_equal(out, dense_out) and np.array_equal(lse, dense_lse)
