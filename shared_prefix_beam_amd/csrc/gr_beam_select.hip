@@ -406,6 +406,7 @@ __device__ __forceinline__ void row_candidates(const SelParams &p, int r, bool t
             z = z < a ? a : (z > p.n_edges ? p.n_edges : z);
             e0 = a;
             n = z - a < p.V ? z - a : p.V;          // distinct labels below V
+            n = n < p.max_fanout ? n : p.max_fanout;  // a node's first max_fanout edges
             n = n < cap ? n : cap;
         }
     }

@@ -102,3 +102,53 @@ def test_last_level_few_candidates():
     ti = I.trie_select_inputs([300, 200], [400, 150], 8192, 2, tr, seed=52, dead=0.1)
     log("[trie] last level")
     check(ti, 400, "last level")
+
+
+def truncated(tr, level, F):
+    """CSR copy of trie `tr` whose nodes at `level` keep only their first F
+    edges (node ids unchanged): what a call with max_fanout F may consider."""
+    lo, hi = int(tr.level_start[level]), int(tr.level_start[level + 1])
+    ptr, tok, child = [0], [], []
+    for u in range(tr.node_ptr.size - 1):
+        a, z = int(tr.node_ptr[u]), int(tr.node_ptr[u + 1])
+        if lo <= u < hi:
+            z = min(z, a + F)
+        tok.extend(tr.edge_tok[a:z].tolist())
+        child.extend(tr.edge_child[a:z].tolist())
+        ptr.append(len(tok))
+    return (np.asarray(ptr, np.int32), np.asarray(tok, np.int32), np.asarray(child, np.int32))
+
+
+@pytest.mark.parametrize("step", [0, 1])
+def test_max_fanout_below_a_node_fanout(small_trie, step):
+    """max_fanout below some expanded node's child count: such a node offers
+    only its first max_fanout edges (the oracle runs on the trie cut so)."""
+    import torch
+    from shared_prefix_beam_amd import gr_attn
+    tr = small_trie
+    F = max(1, tr.level_fanout(step) * 2 // 3)
+    ti = I.trie_select_inputs([40, 17, 60], [30, 17, 45], tr.V, step, tr, seed=11 + step, dead=0.1)
+    si = ti.sel
+    ptr, tok, child = truncated(tr, step, F)
+    assert (np.diff(ptr) < np.diff(tr.node_ptr)).any()       # some node is cut
+    fan = np.diff(ptr)
+    per_beam = np.where(ti.node_old >= 0, fan[np.maximum(ti.node_old, 0)], 0)
+    ro = si.row_offset_old
+    n_cand = np.array([per_beam[ro[b]:ro[b + 1]].sum() for b in range(len(ro) - 1)], np.int64)
+    K_max = int(np.diff(si.row_offset_new).max())
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+    log(f"[trie] step {step}: max_fanout {F} below the level's {tr.level_fanout(step)}")
+    out = gr_attn.beam_select_trie(
+        i32(si.row_offset_old), i32(si.row_offset_new), torch.from_numpy(si.score_old).cuda(),
+        torch.from_numpy(np.ascontiguousarray(si.logits)).cuda(), i32(ti.node_old),
+        i32(tr.node_ptr), i32(tr.edge_tok), i32(tr.edge_child), K_max, F,
+        R_new=int(si.row_offset_new[-1]))
+    torch.cuda.synchronize()
+    got = tuple(t.cpu().numpy() for t in out)
+    check_against_oracle(
+        si, got, K_max, f"max_fanout {F} step {step}",
+        lambda rw: O.beam_select_trie(ro, rw, si.score_old, si.logits, ti.sid, ptr, tok, child),
+        n_cand=n_cand)
