@@ -212,6 +212,21 @@ def pin_p4_special(fn: StepFn, Hkv: int = 1, D: int = 4):
     _, _, _, _, sk = fn(ro_old, ro_new, parent_eq, path_old, len_old, new_k, new_k, path_init,
                         bk, bv, W_cap)
     assert sk == 1
+    # a negative parent at step 1 (request 2, beam 1)
+    parent_neg = np.array([0, 0, 1, -1, 0], dtype=np.int32)
+    p, _, bk5, _, sk = fn(ro_old, ro_new, parent_neg, path_old, len_old, new_k, new_k, path_init,
+                          bk, bv, W_cap)
+    assert sk == 1
+    assert np.array_equal(p[3], path_init[3]) and list(p[4]) == [2, 6, -3]
+    assert np.array_equal(bk5[2, 5], bk[2, 5])       # its slot keeps its contents
+    # a BeamKV pool of 6 slots: request 2 at step 1 writes slots 4 + k, so its
+    # beam 2 (slot 6) is out of range and writes nothing
+    p, _, bk6, _, sk = fn(ro_old, ro_new, parent, path_old, len_old, new_k, new_k, path_init,
+                          bk[:, :6].copy(), bv[:, :6].copy(), W_cap)
+    assert sk == 1
+    assert list(p[2]) == [3, 4, -3] and list(p[3]) == [2, 5, -3]
+    assert np.array_equal(p[4], path_init[4])
+    assert np.array_equal(bk6[2, 5], new_k[3]) and np.array_equal(bk6[0, :2], new_k[:2])
 
 
 def battery(fn: StepFn) -> List[str]:
