@@ -38,12 +38,9 @@ constexpr int SEL_HEAD_REG = 8;                           // head keys per threa
 constexpr int SEL_SURV_REG = 4;                           // survivors per thread in registers
 constexpr int SEL_SURV_LDS = SEL_SURV_REG * SEL_REQ_THREADS;
 constexpr int SEL_REQ_NV = SEL_MAX_V / SEL_REQ_THREADS;   // logits per thread, re-selection
-// 512 threads of 16 candidates per row for vocabularies up to 8192 (each
-// row's chain is half as long) measured slower than 256 of 32: 8 x 128
-// beams 27.1 -> 28.2 us, 4 x 900 55.1 -> 60.3 us; kept for other builds.
-#ifndef ROW512
-#define ROW512 0
-#endif
+// (512 threads of 16 candidates per row for vocabularies up to 8192, each
+// row's chain half as long, measured slower than 256 of 32: 8 x 128 beams
+// 27.1 -> 28.2 us, 4 x 900 55.1 -> 60.3 us.)
 constexpr int SEL_WCAND = 256;                            // the same, one wave per row
 
 // Order-preserving bits of a float: negative values complemented, the sign
@@ -1188,8 +1185,6 @@ hipError_t launch_beam_select(const SelParams &p, hipStream_t s)
                 hipLaunchKernelGGL((select_rows_wave<4, true>), gw, t, 0, s, p);
             else if (n <= 64 * 16)
                 hipLaunchKernelGGL((select_rows_wave<16, true>), gw, t, 0, s, p);
-            else if (ROW512 && n <= 16 * 2 * SEL_ROW_THREADS)
-                hipLaunchKernelGGL((select_rows<16, 2 * SEL_ROW_THREADS, true>), g, t2, 0, s, p);
             else if (n <= 32 * SEL_ROW_THREADS)
                 hipLaunchKernelGGL((select_rows<32, SEL_ROW_THREADS, true>), g, t, 0, s, p);
             else
@@ -1198,8 +1193,6 @@ hipError_t launch_beam_select(const SelParams &p, hipStream_t s)
             hipLaunchKernelGGL((select_rows_wave<4, false>), gw, t, 0, s, p);
         } else if (n <= 64 * 16) {
             hipLaunchKernelGGL((select_rows_wave<16, false>), gw, t, 0, s, p);
-        } else if (ROW512 && n <= 16 * 2 * SEL_ROW_THREADS) {
-            hipLaunchKernelGGL((select_rows<16, 2 * SEL_ROW_THREADS, false>), g, t2, 0, s, p);
         } else if (n <= 32 * SEL_ROW_THREADS) {
             hipLaunchKernelGGL((select_rows<32, SEL_ROW_THREADS, false>), g, t, 0, s, p);
         } else {
