@@ -87,3 +87,64 @@ def test_metadata_checker():
     v = gr_attn.check_metadata(bad_len, bad_path, dev["beam_len"], dev["row_offset"], **kw)
     torch.cuda.synchronize()
     assert int(v.item()) == 3
+
+
+def count_violations(row_offset, ctx_len, beam_len, beam_path, *, B, R, W_max, ctx_cap, T_cap,
+                     beam_cap):
+    """The documented preconditions of gr_check_metadata, counted per request
+    (row range, context length, path length; plus one for a first offset
+    other than 0 or a last other than R) and per used path entry."""
+    bad = 0
+    for b in range(B):
+        lo, hi = int(row_offset[b]), int(row_offset[b + 1])
+        bad += int(hi < lo or hi - lo > W_max or lo < 0 or hi > R)
+        bad += int(not 0 <= ctx_len[b] <= ctx_cap)
+        bad += int(not 0 <= beam_len[b] <= T_cap)
+    if B > 0:
+        bad += int(row_offset[0] != 0 or row_offset[B] != R)
+    for t in range(R if B > 0 else 0):
+        b = 0
+        while b + 1 < B and row_offset[b + 1] <= t:   # the row's request, as found
+            b += 1
+        T = min(max(int(beam_len[b]), 0), T_cap)
+        bad += int(np.sum((beam_path[t, :T] < 0) | (beam_path[t, :T] >= beam_cap)))
+    return bad
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_metadata_checker_counts_every_rule(seed):
+    """Seeded corruptions of the row offsets, lengths and path entries: the
+    device count equals the count of the documented rules."""
+    import torch
+    from shared_prefix_beam_amd import gr_attn
+    inp = I.generate(I.WORKLOADS[3])
+    rng = np.random.default_rng(600 + seed)
+    ro, cl, bl = inp.row_offset.copy(), inp.ctx_len.copy(), inp.beam_len.copy()
+    bp = inp.beam_path.copy()
+    B, R, T_cap = inp.B, inp.R, bp.shape[1]
+    W_max = int(np.diff(inp.row_offset).max())
+    for _ in range(int(rng.integers(1, 4))):
+        kind = int(rng.integers(0, 6))
+        b = int(rng.integers(0, B))
+        if kind == 0:
+            ro[b + 1] = ro[b] - int(rng.integers(1, 5))          # decreasing
+        elif kind == 1:
+            ro[int(rng.integers(0, B + 1))] += int(rng.integers(1, 40))   # too wide / past R
+        elif kind == 2:
+            cl[b] = -1 if rng.random() < 0.5 else inp.ctx_cap + 1
+        elif kind == 3:
+            bl[b] = -1 if rng.random() < 0.5 else T_cap + 1
+        elif kind == 4:
+            bp[int(rng.integers(0, R)), 0] = -1
+        else:
+            bp[int(rng.integers(0, R)), int(rng.integers(0, T_cap))] = inp.beam_cap
+    kw = dict(B=B, R=R, W_max=W_max, ctx_cap=inp.ctx_cap, T_cap=T_cap, beam_cap=inp.beam_cap)
+    want = count_violations(ro, cl, bl, bp, **kw)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    log(f"[invariant] metadata checker, corruption seed {seed}: {want} violations expected")
+    ckw = {k: x for k, x in kw.items() if k != "T_cap"}   # T_cap: the path table's stride
+    v = gr_attn.check_metadata(dev(cl), dev(bp), dev(bl), dev(ro), Hq=inp.wl.Hq, Hkv=inp.wl.Hkv,
+                               D=inp.wl.D, **ckw)
+    torch.cuda.synchronize()
+    assert int(v.item()) == want
+    assert want > 0 or seed < 0
