@@ -143,3 +143,150 @@ def test_non_default_stream():
     s.synchronize()
     assert np.array_equal(out.float().cpu().numpy(), ref_out)
     assert np.array_equal(lse.cpu().numpy(), ref_lse)
+
+
+def replays_match(call, outs, inputs_a, inputs_b, what):
+    """Eager results of `call` for two input states (set by inputs_a() /
+    inputs_b()), then six replays of one captured call, alternating the
+    states, each checked bitwise; `outs` are the output tensors."""
+    import torch
+    inputs_a()
+    call()
+    torch.cuda.synchronize()
+    ref_a = [o.clone() for o in outs]
+    inputs_b()
+    call()
+    torch.cuda.synchronize()
+    ref_b = [o.clone() for o in outs]
+    assert any(not torch.equal(a, b) for a, b in zip(ref_a, ref_b)), "inputs do not matter"
+    inputs_a()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()                                   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    log(f"[graph] {what} captured")
+    for i in range(6):
+        use_b = i % 2 == 1
+        (inputs_b if use_b else inputs_a)()
+        for o in outs:
+            o.zero_()
+        junk = torch.randn(1 << 20, device="cuda").sum()     # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = ref_b if use_b else ref_a
+        assert all(torch.equal(o, r) for o, r in zip(outs, ref)), f"{what}: replay {i}"
+        del junk
+
+
+def test_beam_select_graph_replays():
+    import torch
+    from shared_prefix_beam_amd import gr_attn
+    si = I.select_inputs([60, 33, 90], [40, 33, 64], 3000, seed=51)
+    d = "cuda"
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(d)
+    ro_old, ro_new = i32(si.row_offset_old), i32(si.row_offset_new)
+    score = torch.from_numpy(si.score_old).to(d)
+    logits = torch.from_numpy(np.ascontiguousarray(si.logits)).to(d)
+    la, lb = logits.clone(), torch.flip(logits, dims=[1]).contiguous()
+    R_new, K_max = int(si.row_offset_new[-1]), 64
+    outs = [torch.empty(R_new, dtype=torch.float32, device=d),
+            torch.empty(R_new, dtype=torch.int32, device=d),
+            torch.empty(R_new, dtype=torch.int32, device=d)]
+    dims = gr_attn.SelectDims(B=3, R_old=logits.shape[0], R_new=R_new, V=logits.shape[1],
+                              K_max=K_max, reserved=0)
+    ws = torch.empty(gr_attn.gr_beam_select_workspace_bytes(dims), dtype=torch.uint8, device=d)
+
+    def call():
+        gr_attn.beam_select(ro_old, ro_new, score, logits, K_max, score_new=outs[0],
+                            parent=outs[1], token=outs[2], workspace=ws)
+    replays_match(call, outs, lambda: logits.copy_(la), lambda: logits.copy_(lb), "beam_select")
+
+
+def test_beam_select_trie_graph_replays():
+    import torch
+    from shared_prefix_beam_amd import gr_attn
+    tr = I.build_trie(I.sid_catalog(3000, 3, 300, seed=31), 300)
+    ti = I.trie_select_inputs([40, 17, 60], [30, 17, 45], tr.V, 1, tr, seed=52, dead=0.1)
+    si = ti.sel
+    d = "cuda"
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(d)
+    args = [i32(si.row_offset_old), i32(si.row_offset_new), torch.from_numpy(si.score_old).to(d)]
+    logits = torch.from_numpy(np.ascontiguousarray(si.logits)).to(d)
+    la, lb = logits.clone(), torch.flip(logits, dims=[1]).contiguous()
+    trie = [i32(ti.node_old), i32(tr.node_ptr), i32(tr.edge_tok), i32(tr.edge_child)]
+    R_new, K_max = int(si.row_offset_new[-1]), 45
+    outs = [torch.empty(R_new, dtype=torch.float32, device=d)] + \
+        [torch.empty(R_new, dtype=torch.int32, device=d) for _ in range(3)]
+    dims = gr_attn.SelectDims(B=3, R_old=logits.shape[0], R_new=R_new, V=logits.shape[1],
+                              K_max=K_max, reserved=0)
+    ws = torch.empty(gr_attn.gr_beam_select_workspace_bytes(dims), dtype=torch.uint8, device=d)
+
+    def call():
+        gr_attn.beam_select_trie(*args, logits, *trie, K_max, max(tr.level_fanout(1), 1),
+                                 score_new=outs[0], parent=outs[1], token=outs[2],
+                                 node_new=outs[3], workspace=ws)
+    replays_match(call, outs, lambda: logits.copy_(la), lambda: logits.copy_(lb),
+                  "beam_select_trie")
+
+
+def attention_case():
+    import torch
+    inp = I.custom(B=3, Hq=16, Hkv=8, D=128, W=[37, 5, 70], ctx_len=[1000, 33, 517],
+                   beam_len=[3, 1, 5], seed=53)
+    t = I.to_torch(inp)
+    q_a, q_b = t["q"].clone(), torch.randn_like(t["q"].float()).to(torch.bfloat16)
+    outs = [torch.empty_like(t["q"]),
+            torch.empty(t["q"].shape[:2], dtype=torch.float32, device="cuda")]
+    return inp, t, q_a, q_b, outs
+
+
+def test_paged_graph_replays():
+    import torch
+    from shared_prefix_beam_amd import gr_attn
+    inp, t, q_a, q_b, outs = attention_case()
+    pg = I.to_paged(inp, 48, seed=54)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+        torch.bfloat16).cuda()
+    kp, vp = bf(pg.k_pages), bf(pg.v_pages)
+    tab = torch.from_numpy(pg.page_table.astype(np.int32)).cuda()
+    W_max, tiling = int(max(inp.wl.W)), (4, 1, 3)
+    dims = gr_attn.make_dims(t["q"], t["ctx_k"], t["beam_k"], t["beam_path"], W_max,
+                             tiling=tiling)
+    ws = torch.zeros(gr_attn.gr_decode_attn_workspace_bytes(dims), dtype=torch.uint8,
+                     device="cuda")
+
+    def call():
+        gr_attn.decode_attn_paged(t["q"], kp, vp, tab, 48, t["ctx_len"], t["beam_k"],
+                                  t["beam_v"], t["beam_path"], t["beam_len"], t["row_offset"],
+                                  W_max=W_max, ctx_cap=inp.ctx_cap, out=outs[0], lse=outs[1],
+                                  workspace=ws, tiling=tiling)
+    replays_match(call, outs, lambda: t["q"].copy_(q_a), lambda: t["q"].copy_(q_b),
+                  "decode_attn_paged")
+
+
+def test_noalloc_graph_replays():
+    import torch
+    from shared_prefix_beam_amd import gr_attn
+    inp, t, q_a, q_b, outs = attention_case()
+    W_max = int(max(inp.wl.W))
+    dims = gr_attn.make_dims(t["q"], t["ctx_k"], t["beam_k"], t["beam_path"], W_max,
+                             tiling=(4, 1, 3))
+    st = torch.cuda.current_stream()
+    args = [gr_attn._ptr(x) for x in (t["row_offset"], t["q"], t["ctx_k"], t["ctx_v"],
+                                      t["ctx_len"], t["beam_k"], t["beam_v"], t["beam_path"],
+                                      t["beam_len"], outs[0], outs[1])]
+
+    def call():
+        s = torch.cuda.current_stream()
+        assert gr_attn.gr_decode_attn_noalloc(dims, *args, s.cuda_stream) == gr_attn.GR_OK
+    call()                                        # first call on the device: scratch set up
+    torch.cuda.synchronize()
+    del st
+    replays_match(call, outs, lambda: t["q"].copy_(q_a), lambda: t["q"].copy_(q_b),
+                  "decode_attn_noalloc")
