@@ -290,3 +290,47 @@ def test_noalloc_graph_replays():
     del st
     replays_match(call, outs, lambda: t["q"].copy_(q_a), lambda: t["q"].copy_(q_b),
                   "decode_attn_noalloc")
+
+
+def test_concurrent_streams():
+    """Two streams (default priority) run calls at the same time, each with
+    its own inputs, outputs and workspace: every result equals its eager
+    call's, bitwise."""
+    import torch
+    from shared_prefix_beam_amd import gr_attn
+    cases = []
+    for k, (W, L, tiling) in enumerate(((([37, 5, 70]), [1000, 33, 517], (4, 1, 3)),
+                                        (([90, 64]), [700, 1300], None))):
+        inp = I.custom(B=len(W), Hq=16, Hkv=8, D=128, W=W, ctx_len=L,
+                       beam_len=[3] * len(W), seed=60 + k)
+        t = I.to_torch(inp)
+        W_max = int(max(W))
+        dims = gr_attn.make_dims(t["q"], t["ctx_k"], t["beam_k"], t["beam_path"], W_max,
+                                 tiling=tiling)
+        ws = torch.zeros(max(gr_attn.gr_decode_attn_workspace_bytes(dims), 256),
+                         dtype=torch.uint8, device="cuda")
+        cases.append((t, W_max, tiling, ws))
+
+    def run(case, out=None, lse=None):
+        t, W_max, tiling, ws = case
+        return gr_attn.decode_attn(t["q"], t["ctx_k"], t["ctx_v"], t["ctx_len"], t["beam_k"],
+                                   t["beam_v"], t["beam_path"], t["beam_len"], t["row_offset"],
+                                   W_max=W_max, out=out, lse=lse, workspace=ws, tiling=tiling)
+    refs = []
+    for c in cases:
+        o, l = run(c)
+        torch.cuda.synchronize()
+        refs.append((o.clone(), l.clone()))
+    streams = [torch.cuda.Stream() for _ in cases]
+    outs = [[(torch.empty_like(r[0]), torch.empty_like(r[1])) for _ in range(8)] for r in refs]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    log("[streams] two streams at once")
+    for i in range(8):                           # interleaved launches on both streams
+        for c, s, o in zip(cases, streams, outs):
+            with torch.cuda.stream(s):
+                run(c, out=o[i][0], lse=o[i][1])
+    torch.cuda.synchronize()
+    for r, o in zip(refs, outs):
+        for i in range(8):
+            assert torch.equal(o[i][0], r[0]) and torch.equal(o[i][1], r[1]), f"call {i}"
