@@ -322,3 +322,24 @@ def test_explicit_scale():
         inp.q, inp.ctx_k, inp.ctx_v, inp.ctx_len, inp.beam_k, inp.beam_v, inp.beam_path,
         inp.beam_len, inp.row_offset, scale=0.05)
     assert_parity(out, lse, ref_out, ref_lse, "scale0.05")
+
+
+@pytest.mark.parametrize("tiling", [None, (4, 1, 1), (4, 2, 1, True)], ids=["planner", "q4_k1", "row16"])
+def test_many_small_requests(tiling):
+    """129 requests of 0-6 beams (1032 (request, KV head) pairs, not a
+    multiple of the 8 XCDs), contexts of 0-300 tokens and 0-4 path tokens:
+    every row against the oracle, and paged bitwise equal to dense."""
+    from test_gpu_paged import run_paged
+    rng = np.random.default_rng(129)
+    B = 129
+    W = [int(x) for x in rng.integers(0, 7, size=B)]
+    L = [int(x) for x in rng.integers(0, 301, size=B)]
+    T = [int(x) for x in rng.integers(0, 5, size=B)]
+    inp = I.custom(B=B, Hq=16, Hkv=8, D=128, W=W, ctx_len=L, beam_len=T, seed=129)
+    log(f"[parity] many small requests B={B} R={inp.R} tiling {tiling}")
+    out, lse = run_lib(inp, "fused", tiling=tiling)
+    ref_out, ref_lse = O.decode_attn_inputs(inp)
+    assert_parity(out, lse, ref_out, ref_lse, f"many requests {tiling}")
+    pg = I.to_paged(inp, 32, seed=130)
+    p_out, p_lse = run_paged(inp, pg, tiling=tiling)
+    assert np.array_equal(p_out, out) and np.array_equal(p_lse, lse), "paged and dense differ"
