@@ -40,3 +40,15 @@ def test_random_selection(seed):
     si = I.select_inputs(W_old, W_new, V, seed, **kw)
     log(f"[select random {seed}] W_old={W_old} W_new={W_new} V={V} K_max={K_max} {kw}")
     check_against_oracle(si, run_gpu(si, K_max), K_max, f"random {seed}")
+
+
+def test_many_small_requests():
+    """150 requests of 0-8 beams before and 0-12 kept (one request-stage
+    workgroup each), against the oracle."""
+    rng = np.random.default_rng(150)
+    W_old = [int(x) for x in rng.integers(0, 9, size=150)]
+    W_new = [int(x) for x in rng.integers(0, 13, size=150)]
+    si = I.select_inputs(W_old, W_new, 700, 150)
+    K_max = max(W_new)
+    log(f"[select] 150 small requests, V=700, K_max={K_max}")
+    check_against_oracle(si, run_gpu(si, K_max), K_max, "150 small requests")

@@ -45,3 +45,20 @@ def test_random_step(seed):
     args = (s.row_offset, st.row_offset_new, st.parent, s.beam_path, s.beam_len, st.new_k,
             st.new_v, path_init, s.beam_k, s.beam_v, s.W_cap)
     assert_same(gpu_step(*args), O.beam_step(*args), f"random step {seed}")
+
+
+def test_many_small_requests_step():
+    """120 requests of 0-8 beams before and after the step, bit-exact."""
+    rng = np.random.default_rng(120)
+    B = 120
+    W_old = [int(x) for x in rng.integers(0, 9, size=B)]
+    W_new = [int(x) for x in rng.integers(0, 9, size=B)]
+    beam_len = [int(x) for x in rng.integers(0, 5, size=B)]
+    st = I.step_inputs(B=B, Hkv=8, D=128, W_old=W_old, W_new=W_new, beam_len=beam_len, seed=121,
+                       T_cap=5, W_cap=9)
+    log("[step] 120 small requests")
+    s = st.state
+    path_init = np.full((st.R_new, s.T_cap), -1, dtype=np.int32)
+    args = (s.row_offset, st.row_offset_new, st.parent, s.beam_path, s.beam_len, st.new_k,
+            st.new_v, path_init, s.beam_k, s.beam_v, s.W_cap)
+    assert_same(gpu_step(*args), O.beam_step(*args), "120 small requests")
