@@ -1,7 +1,7 @@
 #!/bin/bash
-# Build the host-side C ABI (gr_attn_api.cpp), the C oracle and the driver
+# Build the host-side C ABI (gr_attn_api.cpp), the C oracle and the test program
 # with AddressSanitizer and UndefinedBehaviorSanitizer (g++ only: no device
-# code), then run the driver.  Usage: build_and_run.sh OUT_DIR
+# code), then run the test program.  Usage: build_and_run.sh OUT_DIR
 set -euo pipefail
 here="$(cd "$(dirname "$0")" && pwd)"
 root="$(cd "$here/../.." && pwd)"

@@ -3,7 +3,7 @@
 // under AddressSanitizer and UndefinedBehaviorSanitizer and run on a machine
 // without a GPU.  The device queries report one gfx950 device; every
 // launcher checks the launch it is given against the buffers the caller
-// passed (recorded by the driver in `g_call`) and enqueues nothing.
+// passed (recorded for the test program in `g_call`) and enqueues nothing.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>

@@ -1,4 +1,4 @@
-// Sanitizer driver for the host-side C code: argument validation, the work
+// Sanitizer test program for the host-side C code: argument validation, the work
 // decomposition and workspace layout of gr_attn_api.cpp (through the C ABI,
 // with the launchers stubbed: they check each planned launch against the
 // caller's buffers), and the C oracle on small random inputs.  Built with

@@ -1,4 +1,4 @@
-// What the sanitizer driver tells the launch stubs about the current call.
+// What the sanitizer test program tells the launch stubs about the current call.
 #pragma once
 #include <cstddef>
 #include <cstdint>
