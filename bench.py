@@ -246,21 +246,25 @@ def write_profile_summaries(d: str):
                   open(os.path.join(out_dir, f"traffic_{name}.json"), "w"), indent=1)
         print(f"wrote profiles/{name}.txt", flush=True)
     write_step_profile(d, f_fetch, f_write, copy_fetch_kib, copy_write_kib)
+    write_step_profile(d, f_fetch, f_write, copy_fetch_kib, copy_write_kib, w="beam_step2")
     write_select_profile(d, f_fetch, f_write)
+    write_select_profile(d, f_fetch, f_write, w="select2")
     write_select_profile(d, f_fetch, f_write, w="trie")
 
 
-def write_step_profile(d, f_fetch, f_write, copy_fetch_kib, copy_write_kib):
-    """The same summary for the beam-step kernel (profiled with --only beam_step)."""
-    if not os.path.isdir(os.path.join(d, "trace_beam_step")):
+def write_step_profile(d, f_fetch, f_write, copy_fetch_kib, copy_write_kib, w="beam_step"):
+    """The same summary for the beam-step kernel (profiled with --only beam_step for the
+    900-beam shape, --only beam_step2 for the 128-beam one)."""
+    if not os.path.isdir(os.path.join(d, f"trace_{w}")):
         return
-    st = I.step_workload(STEP_CFGS[0])
-    name_wl = I.STEP_WORKLOADS[STEP_CFGS[0]]["name"]
+    cfg = STEP_CFGS[1] if w == "beam_step2" else STEP_CFGS[0]
+    st = I.step_workload(cfg)
+    name_wl = I.STEP_WORKLOADS[cfg]["name"]
     nbytes = algorithmic_step(st)
-    stats = _csv_rows(os.path.join(d, "trace_beam_step"), "kernel_stats.csv")
-    fetch_kib, n_f = _counter_per_dispatch(os.path.join(d, "fetch_beam_step"), "beam_step",
+    stats = _csv_rows(os.path.join(d, f"trace_{w}"), "kernel_stats.csv")
+    fetch_kib, n_f = _counter_per_dispatch(os.path.join(d, f"fetch_{w}"), "beam_step",
                                           "FETCH_SIZE")
-    write_kib, n_w = _counter_per_dispatch(os.path.join(d, "write_beam_step"), "beam_step",
+    write_kib, n_w = _counter_per_dispatch(os.path.join(d, f"write_{w}"), "beam_step",
                                           "WRITE_SIZE")
     traffic = fetch_kib * 1024 * f_fetch + write_kib * 1024 * f_write
     kern = [r for r in stats if "beam_step" in r["Name"]]
@@ -268,15 +272,15 @@ def write_step_profile(d, f_fetch, f_write, copy_fetch_kib, copy_write_kib):
     sha = kernel_hash(STEP_SOURCES)
     lines = [f"# beam_step on {name_wl}", "",
              "kernel trace (rocprofv3 --kernel-trace --stats), command from the repository root:",
-             "    " + PROFILE_COMMANDS["trace"].format(d="gpurun_out/prof", w="beam_step"), "",
+             "    " + PROFILE_COMMANDS["trace"].format(d="gpurun_out/prof", w=w), "",
              f"{'kernel':60s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
     for r in stats:
         lines.append(f"{r['Name'][:60]:60s} {int(r['Calls']):6d} "
                      f"{float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
                      f"{float(r['MaxNs']) / 1e3:9.2f}")
     lines += ["", "HBM counters, one pass each:",
-              "    " + PROFILE_COMMANDS["fetch"].format(d="gpurun_out/prof", w="beam_step"),
-              "    " + PROFILE_COMMANDS["write"].format(d="gpurun_out/prof", w="beam_step"),
+              "    " + PROFILE_COMMANDS["fetch"].format(d="gpurun_out/prof", w=w),
+              "    " + PROFILE_COMMANDS["write"].format(d="gpurun_out/prof", w=w),
               "    (copy calibration as in the attention summaries)", "",
               f"FETCH_SIZE per dispatch   {fetch_kib:12.1f} KiB  (mean of {n_f})",
               f"WRITE_SIZE per dispatch   {write_kib:12.1f} KiB  (mean of {n_w})",
@@ -297,9 +301,10 @@ def write_step_profile(d, f_fetch, f_write, copy_fetch_kib, copy_write_kib):
 
 
 def write_select_profile(d, f_fetch, f_write, w="select"):
-    """Summary of the two beam-selection kernels (profiled with --only select,
-    or --only trie for the constrained call): per-kernel averages and
-    counters, summed per call."""
+    """Summary of the two beam-selection kernels (profiled with --only select
+    for the 900-beam shape, --only select2 for the 128-beam one, or --only trie
+    for the constrained call): per-kernel averages and counters, summed per
+    call."""
     if not os.path.isdir(os.path.join(d, f"trace_{w}")):
         return
     if w == "trie":
@@ -308,8 +313,9 @@ def write_select_profile(d, f_fetch, f_write, w="select"):
         nbytes = algorithmic_trie(ti)
         title, kname = "constrained beam selection", "beam_select_trie"
     else:
-        name_wl = I.SELECT_WORKLOADS[SELECT_CFGS[0]]["name"]
-        nbytes = algorithmic_select(I.select_workload(SELECT_CFGS[0]))
+        cfg = SELECT_CFGS[1] if w == "select2" else SELECT_CFGS[0]
+        name_wl = I.SELECT_WORKLOADS[cfg]["name"]
+        nbytes = algorithmic_select(I.select_workload(cfg))
         title, kname = "beam selection", "beam_select"
     stats = _csv_rows(os.path.join(d, f"trace_{w}"), "kernel_stats.csv")
     sha = kernel_hash(SELECT_SOURCES)
@@ -834,7 +840,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", choices=["primary", "secondary", "cfg1", "cfg2", "cfg3", "cfg4",
-                                       "cfg5", "paged2", "paged4", "beam_step", "select", "trie"],
+                                       "cfg5", "paged2", "paged4", "beam_step", "beam_step2",
+                                       "select", "select2", "trie"],
                     help="time one workload only and print its launch time (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run 10 device copies of 256 MiB (reference for HBM byte counters)")
@@ -868,14 +875,16 @@ def main():
     if args.peaks:
         print(json.dumps(measured_peaks()), flush=True)
         return
-    if args.only in ("select", "trie"):
+    if args.only in ("select", "select2", "trie"):
         r = (measure_select(TRIE_CFGS[0], args.steps, args.warmup, trie=True)
-             if args.only == "trie" else measure_select(SELECT_CFGS[0], args.steps, args.warmup))
+             if args.only == "trie" else
+             measure_select(SELECT_CFGS[1 if args.only == "select2" else 0], args.steps,
+                            args.warmup))
         print(json.dumps({"workload": r["name"], "launch_us": r["launch_ms"] * 1e3,
                           "rank_match": r["rank_match"]}), flush=True)
         return
-    if args.only == "beam_step":
-        r = measure_step(STEP_CFGS[0], args.steps, args.warmup)
+    if args.only in ("beam_step", "beam_step2"):
+        r = measure_step(STEP_CFGS[1 if args.only == "beam_step2" else 0], args.steps, args.warmup)
         print(json.dumps({"workload": r["name"], "launch_us": r["launch_ms"] * 1e3,
                           "bit_exact": r["bit_exact"]}), flush=True)
         return
