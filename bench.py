@@ -544,7 +544,10 @@ def config_entry(cfg: int, r) -> dict:
 
 def measure_step(cfg: int, steps: int, warmup: int):
     """Time gr_beam_step on the step workload `cfg` the way `measure` times
-    the attention: rotating input sets, direct C calls, one event pair."""
+    the attention: rotating input sets, direct C calls, one event pair per
+    region of `steps` launches; five regions, their median reported (the kernel
+    is about as short as one call's host-side cost, so a region in which the
+    host falls behind measures the host)."""
     import torch
     from shared_prefix_beam_amd import gr_attn
 
@@ -583,15 +586,18 @@ def measure_step(cfg: int, steps: int, warmup: int):
 
     for i in range(warmup):
         step(i)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for i in range(steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    launch_ms = ev0.elapsed_time(ev1) / steps
+    reps = []
+    for _ in range(5):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(steps):
+            step(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        reps.append(ev0.elapsed_time(ev1) / steps)
+    launch_ms = sorted(reps)[len(reps) // 2]
     # bit-exact spot check of the first set against the oracle (not timed)
     from oracle import oracle as O
     ref_path, ref_len, ref_k, ref_v, _ = O.beam_step(
@@ -604,7 +610,7 @@ def measure_step(cfg: int, steps: int, warmup: int):
           and np.array_equal(base["beam_v"].view(torch.int16).cpu().numpy().view(np.uint16),
                              ref_v))
     return dict(st=st, name=I.STEP_WORKLOADS[cfg]["name"], nbytes=nbytes, launch_ms=launch_ms,
-                n_sets=n_sets, bit_exact=bool(ok))
+                reps_ms=reps, n_sets=n_sets, bit_exact=bool(ok))
 
 
 def measure_select(cfg: int, steps: int, warmup: int, trie: bool = False):
@@ -734,6 +740,7 @@ def select_entry(r) -> dict:
 def step_entry(r) -> dict:
     gbs = r["nbytes"] / (r["launch_ms"] * 1e-3) / 1e9
     return {"workload": r["name"], "rows": r["st"].R_new, "launch_us": r["launch_ms"] * 1e3,
+            "launch_us_reps": [round(x * 1e3, 3) for x in r["reps_ms"]],
             "value": r["st"].R_new / (r["launch_ms"] * 1e-3), "unit": "beam-rows/s",
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": gbs / PEAK_HBM_GBS,
